@@ -1,0 +1,155 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: PagedAttention decode on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the pages' statement of the problem):
+ *   - The KV cache is a pool of fixed-size blocks, allocated per sequence as it grows and
+ *     not contiguous in memory ("vllm-project-vllm -- L2", section 3 Q2; section 9 "Memory
+ *     Management").  Here a pool is [num_blocks, block_size, num_kv_heads, head_dim],
+ *     row-major, one pool for K and one for V.
+ *   - A block table maps (sequence, logical block) to a physical block id; the GPU only reads
+ *     it (same page, section 6 "KV Cache Block Tables").  Here it is int32
+ *     [num_seqs, max_blocks]; logical token t of sequence b lives in physical block
+ *     block_tables[b][t / block_size] at offset t % block_size.
+ *   - Decode attends one new query token per sequence over that sequence's whole cache
+ *     (same page, section 7: decode reads the full KV cache per layer and is bound by memory
+ *     bandwidth).  Query head h reads KV head h / (num_heads / num_kv_heads).
+ *   - Blocks are extended every decode step (same page, section 6): paged_kv_write stores the
+ *     step's new K/V rows at the slots the allocator handed out (slot = block*block_size +
+ *     offset).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
+ *     nothing, keeps no pointer after returning and never synchronises the device.
+ *   - All launches go to `stream` (a hipStream_t; NULL = the null stream) and are
+ *     asynchronous.  A decode step is paged_kv_write -> paged_attn_decode ->
+ *     (paged_attn_reduce), ordered by the stream.
+ *   - Tensors are dense row-major.  Pointers to K/V pools, query, key/value rows, out and
+ *     tmp_out must be 16-byte aligned; everything else 4-byte (slot_mapping 8-byte).
+ *   - Return value: PKV_OK (0) or a negative pkv_status.  Argument checks happen on the host
+ *     before any launch, so an error return means nothing was enqueued.  PKV_ERR_LAUNCH
+ *     reports a HIP launch failure.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation.
+ *   - Device-resident values (block ids, context lengths, slots) are not read on the host.
+ *     Kernels clamp them so that every access stays inside the buffers the sizes describe:
+ *     a block id outside [0, num_blocks) or a length beyond the table gives an unspecified
+ *     result, never an out-of-bounds access.  With the environment variable PKV_CHECK=1 the
+ *     library instead copies them to the host (synchronising `stream`), validates them and
+ *     returns PKV_ERR_CHECK on a violation.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  FP8_E4M3 is OCP E4M3FN: bias 7, max +-448, NaN = S.1111.111, no inf. */
+typedef enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,       /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,      /* a size is negative, inconsistent or outside the supported set */
+  PKV_ERR_DTYPE = -3,      /* unsupported dtype or dtype combination */
+  PKV_ERR_ALIGN = -4,      /* a pointer is not aligned as required */
+  PKV_ERR_WORKSPACE = -5,  /* split-K buffers missing */
+  PKV_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch */
+  PKV_ERR_CHECK = -7       /* PKV_CHECK=1 found an invalid device-resident value */
+} pkv_status;
+
+/*
+ * paged_kv_write -- scatter this step's new K and V rows into the block pools.
+ *
+ * For every i < num_tokens with s = slot_mapping[i] in [0, num_blocks*block_size):
+ *   key_cache  [s / block_size][s % block_size][:][:] = conv(key  [i][:][:], k_scale)
+ *   value_cache[s / block_size][s % block_size][:][:] = conv(value[i][:][:], v_scale)
+ * Negative slots (padding tokens) and slots past the pool are skipped.  No other byte of
+ * either pool changes.  Two tokens with the same slot: the result is unspecified.
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_dim], src_dtype (PKV_F16 | PKV_BF16)
+ *   key_cache,
+ *   value_cache       [num_blocks, block_size, num_kv_heads, head_dim], cache_dtype
+ *   slot_mapping      [num_tokens] int64
+ *   cache_dtype       == src_dtype: bit copy.  PKV_FP8_E4M3: each element x becomes the
+ *                     E4M3FN code of y = x / scale computed as an IEEE fp32 division, rounded
+ *                     to nearest with ties to the even code; |y| >= 448 (and +-inf) saturate
+ *                     to +-448; NaN gives the NaN code with the sign of y.
+ *   k_scale, v_scale  per-tensor fp32 scales (fp8 cache only; must be finite and > 0)
+ *   head_dim          multiple of 8 (16 for an fp8 cache); num_kv_heads >= 1
+ *
+ * Bit-exact by construction: the same inputs always produce the same pool bytes.
+ */
+int paged_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                   const int64_t* slot_mapping, int num_tokens, int num_blocks, int block_size,
+                   int num_kv_heads, int head_dim, int src_dtype, int cache_dtype, float k_scale,
+                   float v_scale, void* stream);
+
+/*
+ * paged_attn_decode -- one query token per sequence against its paged KV cache.
+ *
+ * For sequence b < num_seqs, query head h < num_heads, with G = num_heads / num_kv_heads,
+ * n = context_lens[b] and K_t, V_t the rows of KV head h / G at logical token t < n:
+ *   s_t = scale * k_scale * (q[b][h] . K_t)                 (K_t as stored)
+ *   out[b][h] = v_scale * sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
+ * n = 0 gives a zero row.  k_scale and v_scale apply to an fp8 cache and must be 1 otherwise.
+ * Tokens at positions >= n (stale tail slots, unused table entries) never influence the
+ * output, whatever bytes they hold.
+ *
+ *   out              [num_seqs, num_heads, head_dim], q_dtype.  Written when partition_size == 0.
+ *   query            [num_seqs, num_heads, head_dim], q_dtype (PKV_F16 | PKV_BF16)
+ *   key_cache,
+ *   value_cache      [num_blocks, block_size, num_kv_heads, head_dim], kv_dtype
+ *   block_tables     [num_seqs, max_blocks] int32; only entries < ceil(n / block_size) are read
+ *   context_lens     [num_seqs] int32
+ *   max_context_len  host-side upper bound of every context_lens[b]; sizes the split-K grid
+ *   partition_size   0: single pass, the output is written directly.
+ *                    > 0: split-K.  Partition p of sequence b covers tokens
+ *                    [p*partition_size, min((p+1)*partition_size, n)).  For every p <
+ *                    ceil(n / partition_size) the kernel writes the partial
+ *                      max_logits[b][h][p] = m_p = max_t s_t
+ *                      exp_sums  [b][h][p] = l_p = sum_t exp(s_t - m_p)
+ *                      tmp_out   [b][h][p] = v_scale * sum_t exp(s_t - m_p) V_t / l_p
+ *                    with Pmax = ceil(max_context_len / partition_size) as the p extent
+ *                    (tmp_out fp32 [num_seqs, num_heads, Pmax, head_dim], the other two fp32
+ *                    [num_seqs, num_heads, Pmax]).  paged_attn_reduce then forms `out`.
+ *                    Must be a multiple of 16 and of block_size.
+ *   Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256; G <= 16;
+ *   (q, kv) dtypes (F16, F16), (BF16, BF16), (BF16, FP8_E4M3), (F16, FP8_E4M3).
+ *
+ * The result is deterministic: identical inputs give bit-identical outputs, and so does any
+ * relabelling of physical blocks that leaves each sequence's logical content unchanged.
+ */
+int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
+                      float v_scale, int max_context_len, int partition_size, float* tmp_out,
+                      float* max_logits, float* exp_sums, void* stream);
+
+/*
+ * paged_attn_reduce -- merge split-K partials by log-sum-exp weighting.
+ *
+ * For every (b, h) with P = ceil(context_lens[b] / partition_size) (clamped to Pmax):
+ *   M = max_{p<P} m_p,  w_p = l_p * exp(m_p - M),  out[b][h] = sum_p w_p o_p / sum_p w_p
+ * rounded to out_dtype (nearest even).  P = 0 gives a zero row.  Partials with p >= P are
+ * never read.  Buffers and Pmax as in paged_attn_decode.
+ */
+int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
+                      const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
+                      int max_context_len, int partition_size, int out_dtype, void* stream);
+
+/* Bytes of tmp_out + max_logits + exp_sums that split-K needs (0 if partition_size <= 0). */
+size_t paged_attn_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                  int partition_size);
+
+/* Static English text for a pkv_status value. */
+const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,38 @@
+"""Builds libpagedkv.so in-tree with hipcc for gfx950 (MI355X)."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = [os.path.join(HERE, "csrc", "pagedkv.hip")]
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "libpagedkv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+    # keep hipcc from emitting packed-fp32 VALU ops (v_pk_{add,mul,fma}_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libpagedkv.so (always recompiles)."""
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, *SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "packed-fp32-ops' is not a recognized feature"
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

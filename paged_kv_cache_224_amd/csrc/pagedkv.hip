@@ -1,0 +1,756 @@
+// pagedkv.hip -- PagedAttention decode, split-K reduce and KV-write kernels for gfx950
+// (AMD Instinct MI355X, CDNA4), behind the C ABI declared in include/pagedkv.h.
+//
+// What is computed is fixed by the pages: the KV cache is a pool of fixed-size blocks reached
+// through a per-sequence block table ("vllm-project-vllm -- L2", section 3 Q2, section 6
+// "KV Cache Block Tables"); decode reads the whole cache of every sequence for one new query
+// token and is bound by memory bandwidth (same page, section 7).  How it is computed here is
+// designed for CDNA4:
+//
+//  * Work unit = one wave (64 lanes) per (sequence b, KV head g, token partition p).  The G
+//    query heads that share KV head g are the 16 columns of the MFMA tiles, so every K/V byte
+//    is read from HBM once and used by all G heads.
+//  * A tile is 16 consecutive tokens of one KV head, always inside one physical block (block
+//    sizes are multiples of 16).  Scores S^T[16 tok x 16 head] = K[16 x D] . Q^T[D x 16] use
+//    v_mfma_f32_16x16x32_{bf16,f16}; each lane loads its A-operand slice of K straight from
+//    HBM with 16-byte loads.  Which physical d feeds which MFMA k-index is free (the sum over
+//    d does not care), so loads are laid out for coalescing and q is loaded to match.
+//  * Online softmax in the exp2 domain on the MFMA output layout: lane l holds 4 tokens of
+//    head l%16, so the tile max needs two cross-lane steps and the running sum stays
+//    lane-local until the end.  Tokens past the context are removed by select, never by
+//    multiplying, and their V rows are zeroed, so stale NaN bytes cannot leak in.
+//  * O^T[D x 16 head] += V^T[D x 16 tok] . P^T[16 tok x 16 head] with v_mfma_f32_16x16x16.
+//    V is staged through LDS in an XOR-swizzled layout and read back with gfx950's
+//    ds_read_b64_tr_b16, which hands each lane 4 tokens of one d: exactly the operand layout.
+//    Computing O^T (not O) keeps head = lane%16 in the accumulator, so the softmax rescale
+//    factor is lane-local too.
+//  * fp8 (OCP E4M3FN) caches are decoded to bf16/f16 in registers with
+//    v_cvt_scalef32_pk_{bf16,f16}_fp8 (exact: every E4M3FN value is representable); the
+//    per-tensor scales are folded into the softmax exponent and the output normalisation.
+//  * The next tile's loads are issued before the current tile is computed.
+//  * Split-K: partials (m, l, o) per partition, merged by paged_attn_reduce with log-sum-exp
+//    weights.  Reduction orders are fixed, so results are deterministic.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "pagedkv.h"
+
+namespace {
+
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+enum { KF16 = PKV_F16, KBF16 = PKV_BF16, KFP8 = PKV_FP8_E4M3 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3: 32-bit data format
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ------------------------------------------------------------------ MFMA wrappers
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ conversions
+
+// Two fp8 codes from the low (HI=false) or high 16 bits of w -> two 16-bit values, packed.
+template <bool BF, bool HI>
+__device__ __forceinline__ unsigned fp8x2_to_16(unsigned w) {
+  if constexpr (BF)
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// 16 fp8 codes (one 16-byte load) -> 16 bf16/f16 values in two 16-byte registers.
+template <bool BF>
+__device__ __forceinline__ void fp8x16_to_16(u32x4 in, u32x4& lo, u32x4& hi) {
+  lo.x = fp8x2_to_16<BF, false>(in.x);
+  lo.y = fp8x2_to_16<BF, true>(in.x);
+  lo.z = fp8x2_to_16<BF, false>(in.y);
+  lo.w = fp8x2_to_16<BF, true>(in.y);
+  hi.x = fp8x2_to_16<BF, false>(in.z);
+  hi.y = fp8x2_to_16<BF, true>(in.z);
+  hi.z = fp8x2_to_16<BF, false>(in.w);
+  hi.w = fp8x2_to_16<BF, true>(in.w);
+}
+
+template <bool BF>
+__device__ __forceinline__ unsigned short f32_to_16(float x) {  // round to nearest even
+  if constexpr (BF)
+    return __builtin_bit_cast(unsigned short, (__bf16)x);
+  else
+    return __builtin_bit_cast(unsigned short, (_Float16)x);
+}
+
+template <bool BF>
+__device__ __forceinline__ float from16(unsigned short h) {
+  if constexpr (BF)
+    return __uint_as_float((unsigned)h << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ unsigned pack2(unsigned short lo, unsigned short hi) {
+  return (unsigned)lo | ((unsigned)hi << 16);
+}
+
+// OCP E4M3FN code of y, nearest-even, saturating at +-448 (written from the format: bias 7,
+// 3 mantissa bits, subnormals m * 2^-9, S.1111.111 = NaN, no infinities).
+__device__ __forceinline__ unsigned e4m3fn_code(float y) {
+  unsigned u = __float_as_uint(y);
+  unsigned sign = (u >> 24) & 0x80u;
+  unsigned a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;           // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;          // |y| >= 448, inf: saturate
+  if (a < 0x3c800000u) {                              // |y| < 2^-6: multiples of 2^-9
+    float t = __uint_as_float(a) * 512.0f;            // exact scaling by 2^9
+    return sign | (unsigned)__builtin_rintf(t);       // ties to even; 8 -> 2^-6 (code 8)
+  }
+  // normal: keep 3 mantissa bits, round the 20 dropped bits to nearest even, rebias 127->7
+  unsigned r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+// ------------------------------------------------------------------ cross-lane helpers
+
+__device__ __forceinline__ float xor_lanes(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// ------------------------------------------------------------------ decode kernel
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;
+  const int32_t* lens;
+  float* tmp_out;
+  float* max_logits;
+  float* exp_sums;
+  int max_blocks;
+  int Hq;
+  int Hkv;
+  int G;
+  int BS;
+  int num_blocks;
+  int PS;     // 0 = single pass
+  int Pmax;
+  int tile_shift;  // log2(BS / 16)
+  float c2;   // scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// Compile-time geometry of one 16-token tile.
+template <int D, int KV>
+struct Tile {
+  static constexpr int ESZ = (KV == KFP8) ? 1 : 2;         // bytes per cached element
+  static constexpr int ROWB = D * ESZ;                      // bytes of one (token, head) row
+  static constexpr int NS = D / 32;                         // QK k-steps (16x16x32)
+  static constexpr int NT = D / 16;                         // PV d-tiles (16x16x16)
+  static constexpr int KLD = (KV == KFP8) ? NS / 2 : NS;    // 16-byte K loads per lane
+  static constexpr int CPRS = ROWB / 16;                    // 16-byte chunks per source row
+  static constexpr int VLD = ROWB / 64;                     // 16-byte V loads per lane
+  static constexpr int TPI = 64 / CPRS;                     // tokens covered by one V load
+  static constexpr int CPR = D / 8;                         // 16-byte chunks per LDS row (16-bit)
+  static constexpr int LDS_BYTES = 16 * D * 2;
+};
+
+// LDS slot (16-byte unit) of chunk c of token row t; XOR swizzle spreads the transposed
+// reads of 8 consecutive tokens over distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int lds_slot(int t, int c) {
+  const int swz = (CPR == 16) ? ((2 * t) & 15) : (t & 6);
+  return t * CPR + (c ^ swz);
+}
+
+template <int D, int KV, bool BF>
+__global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
+  using TL = Tile<D, KV>;
+  __shared__ __attribute__((aligned(16))) char vtile[TL::LDS_BYTES];
+
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x;
+  const int p = blockIdx.y;
+  const int b = blockIdx.z;
+  const int BS = a.BS;
+
+  int n = a.lens[b];
+  n = n < 0 ? 0 : n;
+  n = min(n, a.max_blocks * BS);
+  int t0 = 0, t1 = n;
+  if (a.PS > 0) {
+    t0 = p * a.PS;
+    if (t0 >= n) return;
+    t1 = min(t0 + a.PS, n);
+  }
+
+  const int hh = lane & 15;     // query head within the group (MFMA column)
+  const int grp = lane >> 4;    // MFMA row group
+  const bool hvalid = hh < a.G;
+  const int h = g * a.G + (hvalid ? hh : 0);
+
+  // ---- q as the B operand of S^T = K . Q^T, d order matching the K loads
+  u32x4 qv[TL::NS];
+  {
+    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + h) * D * 2;
+#pragma unroll
+    for (int s = 0; s < TL::NS; ++s) {
+      int d0;
+      if constexpr (KV == KFP8)
+        d0 = 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
+      else
+        d0 = 32 * s + 8 * grp;
+      u32x4 v = *(const u32x4*)(qrow + d0 * 2);
+      qv[s] = hvalid ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- per-lane byte offsets inside a tile (relative to token 0 of the tile, head g)
+  const int rowstride = a.Hkv * TL::ROWB;    // bytes between consecutive tokens
+  int koff[TL::KLD];
+#pragma unroll
+  for (int i = 0; i < TL::KLD; ++i) koff[i] = (lane & 15) * rowstride + (4 * i + grp) * 16;
+  int voff[TL::VLD];
+  int vslot[TL::VLD];    // LDS byte offset of the (first) 16-bit chunk this load fills
+  int vslot2[TL::VLD];   // fp8 only: the second chunk (16 codes widen to 32 bytes)
+#pragma unroll
+  for (int r = 0; r < TL::VLD; ++r) {
+    const int t = r * TL::TPI + lane / TL::CPRS;
+    const int cs = lane % TL::CPRS;
+    voff[r] = t * rowstride + cs * 16;
+    if constexpr (KV == KFP8) {
+      vslot[r] = lds_slot<TL::CPR>(t, 2 * cs) * 16;
+      vslot2[r] = lds_slot<TL::CPR>(t, 2 * cs + 1) * 16;
+    } else {
+      vslot[r] = lds_slot<TL::CPR>(t, cs) * 16;
+      vslot2[r] = 0;
+    }
+  }
+  int troff[TL::NT];
+  {
+    const int tt = 4 * grp + ((lane >> 2) & 3);
+    const int qq = lane & 3;
+#pragma unroll
+    for (int T = 0; T < TL::NT; ++T)
+      troff[T] = lds_slot<TL::CPR>(tt, 2 * T + (qq >> 1)) * 16 + (qq & 1) * 8;
+  }
+
+  const char* kbase = (const char*)a.kc + (size_t)g * TL::ROWB;
+  const char* vbase = (const char*)a.vc + (size_t)g * TL::ROWB;
+  const size_t blockbytes = (size_t)BS * rowstride;
+  const int tshift = a.tile_shift;                      // log2(BS / 16)
+  const int tmask = (1 << tshift) - 1;
+
+  // Logical block -> physical block id: one scalar load per tile, issued two tiles ahead.
+  // Ids outside [0, num_blocks) are clamped so no access leaves the pool.
+  const int32_t* btrow = a.bt + (size_t)b * a.max_blocks + (t0 >> (tshift + 4));
+  const unsigned nbm1 = (unsigned)(a.num_blocks - 1);
+  auto block_of = [&](int tile) -> int {
+    return (int)min((unsigned)btrow[tile >> tshift], nbm1);
+  };
+  auto tile_ptr_off = [&](int id, int tile) -> size_t {
+    return (size_t)id * blockbytes + (size_t)(tile & tmask) * 16 * rowstride;
+  };
+  // Raw buffer loads: the descriptor base is the tile's first row (scalar), the lane offsets
+  // are fixed VGPRs, and the descriptor's range covers exactly the tile's rows of head g.
+  const int tile_span = 15 * rowstride + TL::ROWB;
+  auto load_tile = [&](size_t off, u32x4* kd, u32x4* vd) {
+    const __amdgpu_buffer_rsrc_t kres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, tile_span, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, tile_span, kBufWord3);
+#pragma unroll
+    for (int i = 0; i < TL::KLD; ++i)
+      kd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 0, 0));
+#pragma unroll
+    for (int r = 0; r < TL::VLD; ++r)
+      vd[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff[r], 0, 0));
+  };
+
+  f32x4 acc[TL::NT];
+#pragma unroll
+  for (int T = 0; T < TL::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
+  float lsum = 0.f;
+
+  // One 16-token tile: scores, online softmax, V^T.P^T accumulation.
+  auto compute = [&](int it, const u32x4* kr, const u32x4* vr) {
+    // -- scores S^T = K . Q^T
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < TL::NS; ++st) {
+      u32x4 kop;
+      if constexpr (KV == KFP8) {
+        u32x4 lo, hi;
+        fp8x16_to_16<BF>(kr[st >> 1], lo, hi);
+        kop = (st & 1) ? hi : lo;
+      } else {
+        kop = kr[st];
+      }
+      s = mfma_16x16x32<BF>(kop, qv[st], s);
+    }
+
+    // -- V tile -> LDS (16-bit, swizzled)
+#pragma unroll
+    for (int r = 0; r < TL::VLD; ++r) {
+      if constexpr (KV == KFP8) {
+        u32x4 lo, hi;
+        fp8x16_to_16<BF>(vr[r], lo, hi);
+        *(u32x4*)(vtile + vslot[r]) = lo;
+        *(u32x4*)(vtile + vslot2[r]) = hi;
+      } else {
+        *(u32x4*)(vtile + vslot[r]) = vr[r];
+      }
+    }
+
+    // -- online softmax (exp2 domain); tokens >= t1 are selected out
+    const int tbase = t0 + (it << 4) + 4 * grp;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (tbase + e < t1) ? s[e] * a.c2 : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, xor_lanes(mx, 16));
+    mx = fmaxf(mx, xor_lanes(mx, 32));
+    if (__ballot(mx > m) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int T = 0; T < TL::NT; ++T) acc[T] *= alpha;
+    }
+    unsigned short ph[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[e] - m));
+      lsum += from16<BF>(ph[e]);
+    }
+    const u32x2 pop = {pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
+
+    // -- O^T += V^T . P^T; V rows of tokens >= t1 are zeroed (stale bytes may be NaN)
+    unsigned vm0 = 0xffffffffu, vm1 = 0xffffffffu;
+    if (t1 - (t0 + (it << 4)) < 16) {
+      vm0 = ((tbase + 0 < t1) ? 0x0000ffffu : 0u) | ((tbase + 1 < t1) ? 0xffff0000u : 0u);
+      vm1 = ((tbase + 2 < t1) ? 0x0000ffffu : 0u) | ((tbase + 3 < t1) ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int T = 0; T < TL::NT; ++T) {
+      s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)vtile + troff[T]));
+      u32x2 vt = __builtin_bit_cast(u32x2, raw);
+      vt.x &= vm0;
+      vt.y &= vm1;
+      acc[T] = mfma_16x16x16<BF>(vt, pop, acc[T]);
+    }
+  };
+
+  const int ntiles = (t1 - t0 + 15) >> 4;
+  if (ntiles > 0) {
+    // Ping-pong over two register sets; the tile after the last is the last one again
+    // (an L2 hit), so every prefetch is unconditional and waits stay in program order.
+    const int last = ntiles - 1;
+    u32x4 kA[TL::KLD], vA[TL::VLD], kB[TL::KLD], vB[TL::VLD];
+    int idA = block_of(0);
+    load_tile(tile_ptr_off(idA, 0), kA, vA);
+    int idB = block_of(min(1, last));
+    int it = 0;
+    for (;;) {
+      load_tile(tile_ptr_off(idB, min(it + 1, last)), kB, vB);
+      idA = block_of(min(it + 2, last));
+      compute(it, kA, vA);
+      if (++it > last) break;
+      load_tile(tile_ptr_off(idA, min(it + 1, last)), kA, vA);
+      idB = block_of(min(it + 2, last));
+      compute(it, kB, vB);
+      if (++it > last) break;
+    }
+  }
+
+  // ---- finish: total sum over the 4 row groups, normalise, store
+  lsum += xor_lanes(lsum, 16);
+  lsum += xor_lanes(lsum, 32);
+  if (!hvalid) return;
+  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+
+  if (a.PS == 0) {
+    unsigned short* orow = (unsigned short*)a.out + ((size_t)b * a.Hq + h) * D;
+#pragma unroll
+    for (int T = 0; T < TL::NT; ++T) {
+      u32x2 w;
+      w.x = pack2(f32_to_16<BF>(acc[T][0] * inv), f32_to_16<BF>(acc[T][1] * inv));
+      w.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
+      *(u32x2*)(orow + 16 * T + 4 * grp) = w;
+    }
+  } else {
+    const size_t prow = ((size_t)b * a.Hq + h) * a.Pmax + p;
+    float* orow = a.tmp_out + prow * D;
+#pragma unroll
+    for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
+    if (grp == 0) {
+      a.max_logits[prow] = m * kLn2;
+      a.exp_sums[prow] = lsum;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ split-K reduce
+
+template <int D, bool BF>
+__global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* tmp_out,
+                                                       const float* max_logits,
+                                                       const float* exp_sums,
+                                                       const int32_t* lens, int Hq, int Pmax,
+                                                       int PS) {
+  constexpr int TPR = D / 4;            // threads per output row (4 floats each)
+  constexpr int SLOTS = 256 / TPR;      // partitions processed side by side
+  __shared__ float red[256];
+  __shared__ f32x4 part[256];
+
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int n = lens[b];
+  n = n < 0 ? 0 : n;
+  const int P = min((n + PS - 1) / PS, Pmax);
+  const size_t row = (size_t)b * Hq + h;
+  unsigned short* orow = (unsigned short*)out + row * D;
+  if (P == 0) {
+    if (tid < TPR) *(u32x2*)(orow + 4 * tid) = u32x2{0u, 0u};
+    return;
+  }
+  const float* ml = max_logits + row * Pmax;
+  const float* es = exp_sums + row * Pmax;
+
+  float mloc = -INFINITY;
+  for (int q = tid; q < P; q += 256) mloc = fmaxf(mloc, ml[q]);
+  red[tid] = mloc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+
+  float wloc = 0.f;
+  for (int q = tid; q < P; q += 256) wloc += es[q] * __builtin_amdgcn_exp2f((ml[q] - M) * kLog2e);
+  red[tid] = wloc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float W = red[0];
+
+  const int dc = tid % TPR, slot = tid / TPR;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int q = slot; q < P; q += SLOTS) {
+    const float w = es[q] * __builtin_amdgcn_exp2f((ml[q] - M) * kLog2e);
+    acc += w * *(const f32x4*)(tmp_out + (row * Pmax + q) * D + 4 * dc);
+  }
+  part[tid] = acc;
+  __syncthreads();
+  if (slot == 0) {
+    f32x4 t = part[dc];
+    for (int s = 1; s < SLOTS; ++s) t += part[s * TPR + dc];
+    const float inv = 1.0f / W;
+    u32x2 w;
+    w.x = pack2(f32_to_16<BF>(t[0] * inv), f32_to_16<BF>(t[1] * inv));
+    w.y = pack2(f32_to_16<BF>(t[2] * inv), f32_to_16<BF>(t[3] * inv));
+    *(u32x2*)(orow + 4 * dc) = w;
+  }
+}
+
+// ------------------------------------------------------------------ KV write scatter
+
+// One workgroup per new token; each thread moves 8 elements (16 source bytes) per step.
+template <bool SRC_BF, bool TO_FP8>
+__global__ __launch_bounds__(256) void kv_write_kernel(const void* key, const void* value,
+                                                      void* key_cache, void* value_cache,
+                                                      const int64_t* slots, long long nslots,
+                                                      int row_elems, float k_scale,
+                                                      float v_scale) {
+  const int i = blockIdx.x;
+  const long long s = slots[i];
+  if (s < 0 || s >= nslots) return;
+  const int chunks = row_elems >> 3;
+  for (int c = threadIdx.x; c < 2 * chunks; c += 256) {
+    const bool isv = c >= chunks;
+    const int cc = isv ? c - chunks : c;
+    const u32x4 x = *(const u32x4*)((const char*)(isv ? value : key) +
+                                    ((size_t)i * row_elems + (size_t)cc * 8) * 2);
+    char* cache = (char*)(isv ? value_cache : key_cache);
+    if constexpr (!TO_FP8) {
+      *(u32x4*)(cache + ((size_t)s * row_elems + (size_t)cc * 8) * 2) = x;
+    } else {
+      const float sc = isv ? v_scale : k_scale;
+      unsigned codes[8];
+      const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned short hbits = (unsigned short)(w[e >> 1] >> (16 * (e & 1)));
+        const float v = from16<SRC_BF>(hbits);
+        codes[e] = e4m3fn_code(v / sc);                 // IEEE fp32 division
+      }
+      u32x2 o;
+      o.x = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
+      o.y = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
+      *(u32x2*)(cache + (size_t)s * row_elems + (size_t)cc * 8) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host helpers
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool check_mode() {
+  const char* e = getenv("PKV_CHECK");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+int pmax_of(int max_context_len, int partition_size) {
+  return partition_size > 0 ? (max_context_len + partition_size - 1) / partition_size : 0;
+}
+
+template <int D, int KV, bool BF>
+void launch_decode(const DecodeParams& p, int B, hipStream_t st) {
+  dim3 grid(p.Hkv, p.PS > 0 ? p.Pmax : 1, B);
+  hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF>), grid, dim3(64), 0, st, p);
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is negative, inconsistent or unsupported";
+    case PKV_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case PKV_ERR_ALIGN: return "a pointer is not aligned as required";
+    case PKV_ERR_WORKSPACE: return "split-K workspace buffers missing";
+    case PKV_ERR_LAUNCH: return "HIP kernel launch failed";
+    case PKV_ERR_CHECK: return "checked mode found an invalid device-resident value";
+    default: return "unknown status";
+  }
+}
+
+size_t paged_attn_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                  int partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+    return 0;
+  const size_t P = (size_t)pmax_of(max_context_len, partition_size);
+  return (size_t)num_seqs * num_heads * P * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+int paged_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                   const int64_t* slot_mapping, int num_tokens, int num_blocks, int block_size,
+                   int num_kv_heads, int head_dim, int src_dtype, int cache_dtype, float k_scale,
+                   float v_scale, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if (src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (cache_dtype != src_dtype && cache_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  const bool to_fp8 = cache_dtype == PKV_FP8_E4M3;
+  if (head_dim % (to_fp8 ? 16 : 8) != 0) return PKV_ERR_SHAPE;
+  if (to_fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  const long long nslots = (long long)num_blocks * block_size;
+  const long long row = (long long)num_kv_heads * head_dim;
+  if (row > (1 << 24)) return PKV_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (check_mode()) {
+    std::vector<int64_t> sm;
+    if (!copy_to_host(sm, slot_mapping, (size_t)num_tokens, st)) return PKV_ERR_LAUNCH;
+    std::vector<char> seen((size_t)nslots, 0);
+    for (int64_t s : sm) {
+      if (s < 0) continue;
+      if (s >= nslots || seen[(size_t)s]) return PKV_ERR_CHECK;
+      seen[(size_t)s] = 1;
+    }
+  }
+  dim3 grid(num_tokens), block(256);
+  const bool bf = src_dtype == PKV_BF16;
+  if (bf && to_fp8)
+    hipLaunchKernelGGL((kv_write_kernel<true, true>), grid, block, 0, st, key, value, key_cache,
+                       value_cache, slot_mapping, nslots, (int)row, k_scale, v_scale);
+  else if (!bf && to_fp8)
+    hipLaunchKernelGGL((kv_write_kernel<false, true>), grid, block, 0, st, key, value, key_cache,
+                       value_cache, slot_mapping, nslots, (int)row, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL((kv_write_kernel<true, false>), grid, block, 0, st, key, value, key_cache,
+                       value_cache, slot_mapping, nslots, (int)row, k_scale, v_scale);
+  return launch_status();
+}
+
+int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
+                      float v_scale, int max_context_len, int partition_size, float* tmp_out,
+                      float* max_logits, float* exp_sums, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks < 0 ||
+      max_context_len < 0 || partition_size < 0)
+    return PKV_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16) return PKV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_SHAPE;
+  if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0) return PKV_ERR_SHAPE;
+  if (partition_size > 0 && (partition_size % block_size != 0)) return PKV_ERR_SHAPE;
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (!(std::isfinite(scale) && std::isfinite(k_scale) && std::isfinite(v_scale)))
+    return PKV_ERR_SHAPE;
+  if (kv_dtype != PKV_FP8_E4M3 && (k_scale != 1.0f || v_scale != 1.0f)) return PKV_ERR_SHAPE;
+  if ((long long)max_blocks * block_size > (1LL << 30)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!query || !key_cache || !value_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (num_blocks == 0 || max_blocks == 0) return PKV_ERR_SHAPE;
+  if (partition_size == 0 && !out) return PKV_ERR_NULL;
+  if (partition_size > 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
+  if (!aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || (out && !aligned(out, 16)) ||
+      (tmp_out && !aligned(tmp_out, 16)) || (max_logits && !aligned(max_logits, 4)) ||
+      (exp_sums && !aligned(exp_sums, 4)))
+    return PKV_ERR_ALIGN;
+  const int Pmax = pmax_of(max_context_len, partition_size);
+  if (partition_size > 0 && Pmax == 0) return PKV_OK;   // every context is empty
+  if (partition_size > 0 && Pmax > 65535) return PKV_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (check_mode()) {
+    std::vector<int32_t> lens, bt;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, st)) return PKV_ERR_LAUNCH;
+    if (!copy_to_host(bt, block_tables, (size_t)num_seqs * max_blocks, st)) return PKV_ERR_LAUNCH;
+    for (int b = 0; b < num_seqs; ++b) {
+      const int n = lens[b];
+      if (n < 0 || n > max_context_len || (long long)n > (long long)max_blocks * block_size)
+        return PKV_ERR_CHECK;
+      for (int j = 0; j < (n + block_size - 1) / block_size; ++j) {
+        const int id = bt[(size_t)b * max_blocks + j];
+        if (id < 0 || id >= num_blocks) return PKV_ERR_CHECK;
+      }
+    }
+  }
+
+  DecodeParams p;
+  p.out = out;
+  p.q = query;
+  p.kc = key_cache;
+  p.vc = value_cache;
+  p.bt = block_tables;
+  p.lens = context_lens;
+  p.tmp_out = tmp_out;
+  p.max_logits = max_logits;
+  p.exp_sums = exp_sums;
+  p.max_blocks = max_blocks;
+  p.Hq = num_heads;
+  p.Hkv = num_kv_heads;
+  p.G = num_heads / num_kv_heads;
+  p.BS = block_size;
+  p.num_blocks = num_blocks;
+  p.PS = partition_size;
+  p.Pmax = Pmax;
+  p.tile_shift = __builtin_ctz((unsigned)block_size) - 4;
+  p.c2 = scale * k_scale * kLog2e;
+  p.v_scale = v_scale;
+
+  const bool bf = q_dtype == PKV_BF16;
+  const bool f8 = kv_dtype == PKV_FP8_E4M3;
+  if (head_dim == 128) {
+    if (f8) { if (bf) launch_decode<128, KFP8, true>(p, num_seqs, st); else launch_decode<128, KFP8, false>(p, num_seqs, st); }
+    else    { if (bf) launch_decode<128, KBF16, true>(p, num_seqs, st); else launch_decode<128, KF16, false>(p, num_seqs, st); }
+  } else {
+    if (f8) { if (bf) launch_decode<64, KFP8, true>(p, num_seqs, st); else launch_decode<64, KFP8, false>(p, num_seqs, st); }
+    else    { if (bf) launch_decode<64, KBF16, true>(p, num_seqs, st); else launch_decode<64, KF16, false>(p, num_seqs, st); }
+  }
+  return launch_status();
+}
+
+int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
+                      const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
+                      int max_context_len, int partition_size, int out_dtype, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size <= 0) return PKV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_SHAPE;
+  if (out_dtype != PKV_F16 && out_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !context_lens) return PKV_ERR_NULL;
+  const int Pmax = pmax_of(max_context_len, partition_size);
+  if (Pmax > 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
+  if (!aligned(out, 16) || (tmp_out && !aligned(tmp_out, 16)) || !aligned(context_lens, 4))
+    return PKV_ERR_ALIGN;
+  if (Pmax > 65535) return PKV_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (check_mode()) {
+    std::vector<int32_t> lens;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, st)) return PKV_ERR_LAUNCH;
+    for (int n : lens)
+      if (n < 0 || n > max_context_len) return PKV_ERR_CHECK;
+  }
+  dim3 grid(num_heads, num_seqs), block(256);
+  const int Pm = Pmax > 0 ? Pmax : 1;
+  const bool bf = out_dtype == PKV_BF16;
+  if (head_dim == 128) {
+    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
+    else    hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
+  } else {
+    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
+    else    hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
+  }
+  return launch_status();
+}
+
+}  // extern "C"

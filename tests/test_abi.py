@@ -1,0 +1,131 @@
+"""The C ABI: the library loads, exports every symbol include/pagedkv.h declares, and rejects
+bad arguments on the host before any launch (no GPU needed).
+
+Every call below fails a host-side check, so no kernel is ever launched with the fake
+pointers used here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_224_amd as pk
+from paged_kv_cache_224_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WS = 0, -1, -2, -3, -4, -5
+A = 0x10000            # an aligned fake pointer value (never dereferenced: every call fails first)
+MIS = 0x10002          # a misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce",
+                          "paged_attn_workspace_bytes", "pkv_status_string"}
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert pk.status_string(0) == "ok"
+    for s in range(-7, 0):
+        assert pk.status_string(s) not in ("ok", "unknown status")
+    assert pk.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    L = pk.lib()
+    assert L.paged_attn_workspace_bytes(64, 32, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
+    assert L.paged_attn_workspace_bytes(8, 32, 128, 131072, 512) == 8 * 32 * 256 * 130 * 4
+    assert L.paged_attn_workspace_bytes(64, 32, 128, 4096, 0) == 0
+
+
+def _decode(**kw):
+    args = dict(out=A, q=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, Hq=8, Hkv=2, D=64, BS=16,
+                NB=80, scale=0.125, qdt=0, kvdt=0, ks=1.0, vs=1.0, maxlen=256, PS=0, tmp=None, ml=None,
+                es=None, stream=None)
+    args.update(kw)
+    return pk.lib().paged_attn_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Hq=6, Hkv=4), E_SHAPE),              # Hq % Hkv != 0
+    (dict(Hq=34, Hkv=2), E_SHAPE),             # group of 17 heads > 16
+    (dict(D=96), E_SHAPE),
+    (dict(BS=48), E_SHAPE),                    # not a power of two
+    (dict(BS=8), E_SHAPE),
+    (dict(PS=24), E_SHAPE),                    # not a multiple of block_size
+    (dict(qdt=2), E_DTYPE),                    # fp8 query
+    (dict(qdt=0, kvdt=1), E_DTYPE),            # f16 q with bf16 cache
+    (dict(ks=2.0), E_SHAPE),                   # scales only for fp8 caches
+    (dict(scale=float("nan")), E_SHAPE),
+    (dict(q=None), E_NULL),
+    (dict(bt=None), E_NULL),
+    (dict(out=None), E_NULL),                  # single pass needs out
+    (dict(PS=64), E_WS),                       # split-K needs the partial buffers
+    (dict(q=MIS), E_ALIGN),
+    (dict(kc=MIS), E_ALIGN),
+    (dict(B=-1), E_SHAPE),
+    (dict(NB=0), E_SHAPE),
+])
+def test_decode_rejects(kw, want):
+    assert _decode(**kw) == want
+
+
+def test_decode_zero_sequences_is_a_noop():
+    assert _decode(B=0, q=None, out=None) == OK
+
+
+def _write(**kw):
+    args = dict(k=A, v=A, kc=A, vc=A, sm=A, T=4, NB=80, BS=16, Hkv=2, D=64, sdt=0, cdt=0, ks=1.0, vs=1.0,
+                stream=None)
+    args.update(kw)
+    return pk.lib().paged_kv_write(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(sdt=2), E_DTYPE),
+    (dict(sdt=0, cdt=1), E_DTYPE),
+    (dict(cdt=2, D=8), E_SHAPE),               # fp8 rows need head_dim % 16 == 0
+    (dict(cdt=2, ks=0.0), E_SHAPE),
+    (dict(cdt=2, vs=float("inf")), E_SHAPE),
+    (dict(T=-1), E_SHAPE),
+    (dict(sm=None), E_NULL),
+    (dict(k=MIS), E_ALIGN),
+    (dict(sm=A + 4), E_ALIGN),
+])
+def test_write_rejects(kw, want):
+    assert _write(**kw) == want
+
+
+def test_write_zero_tokens_is_a_noop():
+    assert _write(T=0, k=None, v=None) == OK
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(PS=0), E_SHAPE),
+    (dict(D=80), E_SHAPE),
+    (dict(odt=2), E_DTYPE),
+    (dict(out=None), E_NULL),
+    (dict(tmp=None), E_WS),
+    (dict(out=MIS), E_ALIGN),
+])
+def test_reduce_rejects(kw, want):
+    args = dict(out=A, tmp=A, ml=A, es=A, lens=A, B=4, Hq=8, D=64, maxlen=256, PS=64, odt=0, stream=None)
+    args.update(kw)
+    assert pk.lib().paged_attn_reduce(*args.values()) == want
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(pk.PagedKVError):
+        _lib._check("paged_attn_decode", E_SHAPE)
