@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark one paged-attention decode step on one MI355X.
+
+A step is the whole hot path over one batch: paged_kv_write of the step's new K/V rows, then
+paged_attn_decode (split-K), then paged_attn_reduce.  Inputs are seeded synthetic tensors
+already resident in HBM.  To keep steps honest about HBM (the 256 MB Infinity Cache would
+otherwise hold part of a 0.6 GB cache between steps), the step rotates over several copies of
+the KV pools, so each step reads pools the previous steps did not touch.
+
+Prints one JSON line: whole-step KV GB/s as `value`, plus decode tokens/s, the decode
+kernel's roofline (algorithmic bytes per launch / its mean HIP-event duration) and the fp64
+CPU oracle timed on this host's cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_cache_224_amd as pk  # noqa: E402
+from paged_kv_cache_224_amd import inputs as I  # noqa: E402
+
+METRIC = "paged decode KV GB/s and % of HBM peak; decode tokens/s, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b", choices=I.CONFIG_ORDER)
+    ap.add_argument("--schedule", default="balanced", choices=["balanced", "fixed", "single"],
+                    help="balanced split-K (default), fixed 512-token partitions, or single pass")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="explicit partition_size (overrides --schedule; <0 = balanced over -N workgroups)")
+    ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
+                    help="only copy a buffer of this size 5 times (reference for HBM traffic counters)")
+    return ap.parse_args()
+
+
+def copy_reference(mib):
+    """Plain device-to-device copies of a known size: the HBM counters of this kernel calibrate
+    FETCH_SIZE / WRITE_SIZE (each copy reads and writes exactly mib MiB)."""
+    n = mib * 2 ** 20 // 4
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_reference_mib": mib, "ms": round(dt * 1e3, 4),
+                      "read_plus_write_gbps": round(2 * mib * 2 ** 20 / dt / 1e9, 1)}), flush=True)
+
+
+def decode_bytes(w):
+    """Algorithmic bytes of one decode launch: KV rows of every (sequence, token) once, q,
+    the used block-table entries and the context lengths (logical and unique-block counts)."""
+    nb = I.algorithmic_bytes(w)
+    cfg = w.cfg
+    e_q = 2
+    base = cfg.B * cfg.Hq * cfg.D * e_q + 4 * int(w.blocks_used.sum()) + 4 * cfg.B
+    return nb["kv_logical"] + base, nb["kv_unique"] + base, nb
+
+
+def cpu_baseline(w, min_seconds):
+    """fp64 oracle (KV write + attention over the whole batch) on this host's cores."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    kvdt = "fp8" if w.cfg.kv_dtype == "fp8" else None
+    if kvdt:
+        kc = oracle.quantize_pool(w.k_pool, w.k_scale)
+        vc = oracle.quantize_pool(w.v_pool, w.v_scale)
+    else:
+        kc, vc = w.k_pool.clone(), w.v_pool.clone()
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.kv_write(w.k_new, w.v_new, kc, vc, w.slot_mapping, w.k_scale, w.v_scale)
+        oracle.attn(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.k_scale, w.v_scale, kvdt,
+                    nthreads=threads)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 50:
+            break
+    t = t_total / reps
+    return t, threads, reps
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "the paged decode path here has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
+    dev = torch.device("cuda:0")
+    cfg = I.CONFIGS[args.workload]
+    if args.partition_size is not None:
+        PS = args.partition_size
+    elif args.schedule == "balanced":
+        PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype],
+                               torch.uint8 if cfg.kv_dtype == "fp8" else I.DTYPES[cfg.kv_dtype])
+    elif args.schedule == "fixed":
+        PS = cfg.partition_size
+    else:
+        PS = 0
+    schedule = "single" if PS == 0 else ("fixed" if PS > 0 else "balanced")
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    w = I.make_workload(cfg)
+    B, Hq, D = cfg.B, cfg.Hq, cfg.D
+    fp8 = cfg.kv_dtype == "fp8"
+
+    # ---- device-resident inputs
+    NB, BS = w.num_blocks, cfg.block_size
+    pool_bytes = 2 * NB * BS * cfg.Hkv * D * (1 if fp8 else 2)
+    copies = args.copies or max(2, math.ceil(1.5 * 2 ** 30 / pool_bytes) + 1)
+    pools = []
+    ksrc = w.k_pool.to(dev)
+    vsrc = w.v_pool.to(dev)
+    for _ in range(copies):
+        if fp8:
+            kc = torch.empty((NB, BS, cfg.Hkv, D), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+            slots = torch.arange(NB * BS, dtype=torch.int64, device=dev)
+            pk.paged_kv_write(ksrc.view(NB * BS, cfg.Hkv, D), vsrc.view(NB * BS, cfg.Hkv, D), kc, vc, slots,
+                              w.k_scale, w.v_scale)
+        else:
+            kc, vc = ksrc.clone(), vsrc.clone()
+        pools.append((kc, vc))
+    del ksrc, vsrc
+    q = w.q.to(dev)
+    k_new, v_new = w.k_new.to(dev), w.v_new.to(dev)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    maxlen = cfg.max_len
+    ws = pk.DecodeWorkspace(B, Hq, D, maxlen, PS, device=dev)
+    out = torch.empty((B, Hq, D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % copies]
+        pk.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
+        if ev is not None:
+            ev[0].record()
+        pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS, ws.tmp_out,
+                             ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale)
+        if ev is not None:
+            ev[1].record()
+        if PS != 0:
+            pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, synchronised on both sides
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = [a.elapsed_time(b) for a, b in evs]
+
+    ms_per_step = 1e3 * wall / args.steps
+
+    dec_logical, dec_unique, nb = decode_bytes(w)
+    step_bytes_unique = nb["decode_unique"] + nb["write"]
+    step_bytes_logical = nb["decode_logical"] + nb["write"]
+    value = step_bytes_unique / (ms_per_step * 1e-3) / 1e9
+    dec_mean_ms = float(np.mean(decode_ms))
+    achieved = dec_unique / (dec_mean_ms * 1e-3) / 1e9
+    tokens_per_s = B / (ms_per_step * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if fp8 else cfg.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "num_seqs": B, "num_heads": Hq, "num_kv_heads": cfg.Hkv, "head_dim": D,
+            "block_size": BS, "context_lens": list(cfg.lens), "sum_context": int(w.context_lens.sum()),
+            "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype, "schedule": schedule, "partition_size": PS,
+            "new_tokens": B,
+            "num_blocks": NB, "pool_copies_rotated": copies,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "decode_kernel_ms_mean": round(dec_mean_ms, 5),
+        "decode_kernel_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(decode_ms, [10, 50, 90])],
+        "step_bytes": {"logical": step_bytes_logical, "unique": step_bytes_unique},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "pa_decode_kernel",
+            "bytes_per_launch": dec_unique,
+        },
+    }
+    if w.prefix_blocks.size:
+        res["logical_gbps"] = round(step_bytes_logical / (ms_per_step * 1e-3) / 1e9, 1)
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        t_cpu, threads, reps = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(step_bytes_unique / t_cpu / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole {cfg.name} batch ({B} sequences): fp64 KV write + attention, mean of {reps} runs "
+                      f"({t_cpu:.3f} s each)",
+            "tokens_per_s": round(B / t_cpu, 2),
+        }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -106,18 +106,29 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
  *   context_lens     [num_seqs] int32
  *   max_context_len  host-side upper bound of every context_lens[b]; sizes the split-K grid
  *   partition_size   0: single pass, the output is written directly.
- *                    > 0: split-K.  Partition p of sequence b covers tokens
- *                    [p*partition_size, min((p+1)*partition_size, n)).  For every p <
- *                    ceil(n / partition_size) the kernel writes the partial
+ *                    > 0: split-K over fixed partitions.  Partition p of sequence b covers
+ *                    tokens [p*partition_size, min((p+1)*partition_size, n)).  For every
+ *                    p < ceil(n / partition_size) the kernel writes the partial
  *                      max_logits[b][h][p] = m_p = max_t s_t
  *                      exp_sums  [b][h][p] = l_p = sum_t exp(s_t - m_p)
  *                      tmp_out   [b][h][p] = v_scale * sum_t exp(s_t - m_p) V_t / l_p
- *                    with Pmax = ceil(max_context_len / partition_size) as the p extent
- *                    (tmp_out fp32 [num_seqs, num_heads, Pmax, head_dim], the other two fp32
- *                    [num_seqs, num_heads, Pmax]).  paged_attn_reduce then forms `out`.
  *                    Must be a multiple of 16 and of block_size.
- *   Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256; G <= 16;
- *   (q, kv) dtypes (F16, F16), (BF16, BF16), (BF16, FP8_E4M3), (F16, FP8_E4M3).
+ *                    < 0: split-K over a balanced schedule: the batch's 16-token tiles, in
+ *                    (sequence, position) order, are cut into W = -partition_size equal
+ *                    contiguous ranges (fewer if a range would drop below 8 tiles), one per
+ *                    workgroup, so every workgroup moves the same number of bytes whatever
+ *                    the length mix.  Each (sequence, range) overlap writes one partial
+ *                    (m, l, o as above, over the tokens of that overlap) at slot
+ *                    p = range - (range of the sequence's first tile).
+ *                    paged_attn_balanced_split() gives the W that fills the device once.
+ *                    In both split-K modes the p extent is Pslots =
+ *                    paged_attn_partial_slots(max_context_len, partition_size): tmp_out is fp32
+ *                    [num_seqs, num_heads, Pslots, head_dim], max_logits and exp_sums fp32
+ *                    [num_seqs, num_heads, Pslots].  paged_attn_reduce, called with the same
+ *                    partition_size, then forms `out`.
+ *   Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256; num_kv_heads <= 16;
+ *   G <= 16; (q, kv) dtypes (F16, F16), (BF16, BF16), (BF16, FP8_E4M3), (F16, FP8_E4M3).
+ *   Every context_lens[b] must be <= max_context_len and <= max_blocks * block_size.
  *
  * The result is deterministic: identical inputs give bit-identical outputs, and so does any
  * relabelling of physical blocks that leaves each sequence's logical content unchanged.
@@ -132,18 +143,28 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
 /*
  * paged_attn_reduce -- merge split-K partials by log-sum-exp weighting.
  *
- * For every (b, h) with P = ceil(context_lens[b] / partition_size) (clamped to Pmax):
+ * For every (b, h), with P the number of partials paged_attn_decode wrote for sequence b
+ * under the same partition_size (ceil(n / partition_size) for fixed partitions; the number of
+ * ranges the sequence's tiles fall in for a balanced split, recomputed from context_lens):
  *   M = max_{p<P} m_p,  w_p = l_p * exp(m_p - M),  out[b][h] = sum_p w_p o_p / sum_p w_p
  * rounded to out_dtype (nearest even).  P = 0 gives a zero row.  Partials with p >= P are
- * never read.  Buffers and Pmax as in paged_attn_decode.
+ * never read.  Buffers and Pslots as in paged_attn_decode.
  */
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                       int max_context_len, int partition_size, int out_dtype, void* stream);
 
-/* Bytes of tmp_out + max_logits + exp_sums that split-K needs (0 if partition_size <= 0). */
+/* Partial slots per (sequence, head) a split-K schedule needs (0 for partition_size == 0). */
+int paged_attn_partial_slots(int max_context_len, int partition_size);
+
+/* Bytes of tmp_out + max_logits + exp_sums that split-K needs (0 if partition_size == 0). */
 size_t paged_attn_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
                                   int partition_size);
+
+/* partition_size (negative) of the balanced split that fills the current HIP device once:
+   -(compute units x decode workgroups resident per unit) for this shape and dtype pair.
+   Returns 0 if no device is available or the shape is unsupported.  Queries the device. */
+int paged_attn_balanced_split(int num_kv_heads, int head_dim, int q_dtype, int kv_dtype);
 
 /* Static English text for a pkv_status value. */
 const char* pkv_status_string(int status);

@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+# PAGEDKV_LIB may name another build of the same library (same ABI); default: the in-tree one.
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 _DT = {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3,
@@ -45,6 +46,10 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_reduce.restype = I
         L.paged_attn_workspace_bytes.argtypes = [I, I, I, I, I]
         L.paged_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.paged_attn_partial_slots.argtypes = [I, I]
+        L.paged_attn_partial_slots.restype = I
+        L.paged_attn_balanced_split.argtypes = [I, I, I, I]
+        L.paged_attn_balanced_split.restype = I
         L.pkv_status_string.argtypes = [I]
         L.pkv_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -96,8 +101,17 @@ def paged_kv_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
 
 def workspace_shapes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
                      partition_size: int):
-    P = max(1, -(-max_context_len // partition_size))
+    """(tmp_out, max_logits/exp_sums) shapes for a split-K schedule (partition_size != 0)."""
+    P = max(1, int(lib().paged_attn_partial_slots(int(max_context_len), int(partition_size))))
     return (num_seqs, num_heads, P, head_dim), (num_seqs, num_heads, P)
+
+
+def balanced_split(num_kv_heads: int, head_dim: int, q_dtype: torch.dtype, kv_dtype: torch.dtype) -> int:
+    """partition_size value (< 0) for the balanced split that fills the current device once."""
+    v = int(lib().paged_attn_balanced_split(num_kv_heads, head_dim, _DT[q_dtype], _DT[kv_dtype]))
+    if v >= 0:
+        raise PagedKVError("paged_attn_balanced_split", v, "no device / unsupported shape")
+    return v
 
 
 def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cache: torch.Tensor,
@@ -144,7 +158,7 @@ class DecodeWorkspace:
     def __init__(self, num_seqs, num_heads, head_dim, max_context_len, partition_size, device="cuda"):
         self.partition_size = partition_size
         self.max_context_len = max_context_len
-        if partition_size > 0:
+        if partition_size != 0:
             so, sm = workspace_shapes(num_seqs, num_heads, head_dim, max_context_len, partition_size)
             self.tmp_out = torch.empty(so, dtype=torch.float32, device=device)
             self.max_logits = torch.empty(sm, dtype=torch.float32, device=device)
@@ -160,6 +174,6 @@ def decode(out: torch.Tensor, query, key_cache, value_cache, block_tables, conte
     paged_attn_decode(out if PS == 0 else None, query, key_cache, value_cache, block_tables, context_lens,
                       scale, ws.max_context_len, PS, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale, v_scale,
                       stream)
-    if PS > 0:
+    if PS != 0:
         paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens, ws.max_context_len, PS,
                           stream)

@@ -151,6 +151,13 @@ __device__ __forceinline__ float xor_lanes(float v, int mask) {
 
 // ------------------------------------------------------------------ decode kernel
 
+enum { MODE_SINGLE = 0, MODE_FIXED = 1, MODE_BALANCED = 2 };
+
+// Balanced split: fewest tiles a workgroup gets (bounds the partial slots per sequence).
+constexpr int kMinChunkTiles = 8;
+// Waves (KV heads) per workgroup; grid.y covers further groups of KV heads.
+constexpr int kMaxWaves = 8;
+
 struct DecodeParams {
   void* out;
   const void* q;
@@ -161,16 +168,20 @@ struct DecodeParams {
   float* tmp_out;
   float* max_logits;
   float* exp_sums;
+  int B;
   int max_blocks;
   int Hq;
   int Hkv;
   int G;
   int BS;
   int num_blocks;
-  int PS;     // 0 = single pass
-  int Pmax;
+  int mode;
+  int PS;          // fixed partitions: tokens per partition
+  int Pslots;      // partial slots per (sequence, head) in the workspace
+  int W;           // balanced: workgroups per head group
+  int cap;         // context lengths are clamped to [0, cap]
   int tile_shift;  // log2(BS / 16)
-  float c2;   // scale * k_scale * log2(e)
+  float c2;        // scale * k_scale * log2(e)
   float v_scale;
 };
 
@@ -197,50 +208,200 @@ __device__ __forceinline__ int lds_slot(int t, int c) {
   return t * CPR + (c ^ swz);
 }
 
+__device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+__device__ __forceinline__ int tiles_of(int n, int cap) { return (clamp_len(n, cap) + 15) >> 4; }
+
+// Balanced split of the batch's (sequence, tile) stream of N tiles into Weff equal ranges:
+// range w is [w*N/Weff, (w+1)*N/Weff); owner_of(t) is the range holding tile t.
+__device__ __forceinline__ int balanced_weff(long long N, int W) {
+  long long cap = N / kMinChunkTiles;
+  long long w = W < cap ? W : cap;
+  return w < 1 ? 1 : (int)w;
+}
+__device__ __forceinline__ long long range_lo(int w, long long N, int Weff) {
+  return (long long)w * N / Weff;
+}
+__device__ __forceinline__ int owner_of(long long t, long long N, int Weff) {
+  return (int)(((t + 1) * Weff + N - 1) / N) - 1;
+}
+
+// A segment: tiles [tlo, thi) of sequence b (n tokens), written to partial `slot` (or, for
+// slot < 0, as the final row).  All fields are wave-uniform.
+struct Seg {
+  int b, tlo, thi, n, slot;
+  long long start;   // balanced split: global index of b's first tile
+  bool valid;
+};
+
+// The ordered list of segments one workgroup processes.  For the balanced split the lengths
+// and tile offsets of 64 consecutive sequences b0 .. b0+63 sit in two VGPRs (lane k holds
+// sequence b0+k), so moving from one segment to the next is register work only; a workgroup
+// whose range runs past b0+63 refills the table.
+struct SegSource {
+  int mode, B, cap, w, Weff;
+  long long N, lo, hi;
+  const int32_t* lens;
+  int b0;               // first sequence of the table
+  long long base;       // global index of sequence b0's first tile
+  int n_v, st_v;        // lane k: clamped length of b0+k, its first tile relative to base
+  unsigned long long vmask;   // lanes whose sequence has a tile inside [lo, hi)
+
+  __device__ __forceinline__ int len(int b) const {
+    return clamp_len(__builtin_amdgcn_readfirstlane(lens[b]), cap);
+  }
+  // Table of sequences b .. b+63 given b's first tile; n_lane = len(b + lane) if already known.
+  __device__ __forceinline__ void fill(int b, long long start, int lane, int n_lane) {
+    b0 = b;
+    base = start;
+    n_v = n_lane;
+    const int t = (n_v + 15) >> 4;
+    int incl = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    st_v = incl - t;
+    const long long s0 = start + st_v;
+    vmask = __ballot(t > 0 && s0 < hi && s0 + t > lo);
+  }
+  __device__ __forceinline__ void fill_load(int b, long long start, int lane) {
+    const int bb = b + lane;
+    fill(b, start, lane, bb < B ? clamp_len(lens[bb], cap) : 0);
+  }
+  __device__ __forceinline__ Seg make_lane(int k) const {
+    Seg s;
+    s.b = b0 + k;
+    s.n = __builtin_amdgcn_readlane(n_v, k);
+    s.start = base + __builtin_amdgcn_readlane(st_v, k);
+    const long long nt = (s.n + 15) >> 4;
+    const long long a = lo > s.start ? lo : s.start;
+    const long long e = hi < s.start + nt ? hi : s.start + nt;
+    s.tlo = (int)(a - s.start);
+    s.thi = (int)(e - s.start);
+    s.slot = w - owner_of(s.start, N, Weff);
+    s.valid = true;
+    return s;
+  }
+  // The first segment at or after table lane k, refilling the table past its end.
+  __device__ __forceinline__ Seg from_lane(int k, int lane) {
+    for (;;) {
+      const unsigned long long m = k < 64 ? (vmask >> k) << k : 0ull;
+      if (m) return make_lane(__builtin_ctzll(m));
+      // nothing left in this table: does the range continue past sequence b0+63?
+      const int n63 = __builtin_amdgcn_readlane(n_v, 63);
+      const long long next_start = base + __builtin_amdgcn_readlane(st_v, 63) + ((n63 + 15) >> 4);
+      if (b0 + 64 >= B || next_start >= hi) {
+        Seg r;
+        r.valid = false;
+        return r;
+      }
+      fill_load(b0 + 64, next_start, lane);
+      k = 0;
+    }
+  }
+  // The segment after s (balanced split only; the other schedules have one segment).
+  __device__ __forceinline__ Seg next(const Seg& s, int lane) {
+    Seg r;
+    r.valid = false;
+    if (mode != MODE_BALANCED) return r;
+    return from_lane(s.b - b0 + 1, lane);
+  }
+};
+
+// One workgroup = up to kMaxWaves waves; wave i handles KV head g = blockIdx.y*kMaxWaves + i,
+// so the waves stream whole blocks ([BS][Hkv][D] is contiguous) together.  Each wave owns one
+// LDS tile and runs one continuous tile pipeline over all segments of its workgroup: the next
+// tile's loads go out while the current tile is computed, also across segment boundaries,
+// and the next segment's q and the next 64-entry window of block ids are loaded one segment
+// (one window) ahead, so a segment switch costs no memory round trip.
 template <int D, int KV, bool BF>
-__global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void pa_decode_kernel(DecodeParams a) {
   using TL = Tile<D, KV>;
-  __shared__ __attribute__((aligned(16))) char vtile[TL::LDS_BYTES];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.y * kMaxWaves + wl;               // KV head of this wave
+  if (g >= a.Hkv) return;
+  char* vtile = smem + wl * TL::LDS_BYTES;
+  const int cap = a.cap;
 
-  const int lane = threadIdx.x;
-  const int g = blockIdx.x;
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
-  const int BS = a.BS;
-
-  int n = a.lens[b];
-  n = n < 0 ? 0 : n;
-  n = min(n, a.max_blocks * BS);
-  int t0 = 0, t1 = n;
-  if (a.PS > 0) {
-    t0 = p * a.PS;
-    if (t0 >= n) return;
-    t1 = min(t0 + a.PS, n);
+  // ---- the workgroup's segments
+  SegSource src;
+  src.mode = a.mode;
+  src.B = a.B;
+  src.cap = cap;
+  src.lens = a.lens;
+  src.w = 0;
+  src.Weff = 1;
+  src.N = 1;
+  src.lo = 0;
+  src.hi = 0;
+  Seg cur;
+  if (a.mode == MODE_SINGLE) {
+    cur.b = blockIdx.x;
+    cur.n = src.len(cur.b);
+    cur.tlo = 0;
+    cur.thi = (cur.n + 15) >> 4;
+    cur.slot = -1;
+    cur.start = 0;
+    cur.valid = true;
+  } else if (a.mode == MODE_FIXED) {
+    cur.b = blockIdx.z;
+    cur.n = src.len(cur.b);
+    cur.slot = blockIdx.x;
+    cur.tlo = (cur.slot * a.PS) >> 4;
+    cur.thi = (min((cur.slot + 1) * a.PS, cur.n) + 15) >> 4;
+    cur.start = 0;
+    cur.valid = cur.thi > cur.tlo;
+    if (!cur.valid) return;
+  } else {
+    // equal contiguous ranges of the batch's (sequence, tile) stream
+    const int B = a.B;
+    const int per = (B + 63) >> 6;                      // sequences per lane in the scan
+    int run = 0, n_first = 0;
+    for (int i = 0; i < per; ++i) {
+      const int bb = lane * per + i;
+      const int n = bb < B ? clamp_len(a.lens[bb], cap) : 0;
+      if (i == 0) n_first = n;
+      run += (n + 15) >> 4;
+    }
+    int incl = run;                                     // inclusive scan over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    const long long N = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    if (N == 0) return;
+    const int Weff = balanced_weff(N, a.W);
+    const int w = blockIdx.x;
+    if (w >= Weff) return;
+    src.w = w;
+    src.Weff = Weff;
+    src.N = N;
+    src.lo = range_lo(w, N, Weff);
+    src.hi = range_lo(w + 1, N, Weff);
+    if (per == 1) {
+      src.fill(0, 0, lane, n_first);                    // the scan already holds every length
+    } else {
+      // the lane whose run of sequences holds tile `lo` starts the table
+      const unsigned long long hit = __ballot(incl > src.lo);
+      if (hit == 0) return;                             // unreachable for lo < N
+      const int L = __builtin_ctzll(hit);
+      src.fill_load(L * per, __builtin_amdgcn_readfirstlane(__shfl(incl - run, L, 64)), lane);
+    }
+    cur = src.from_lane(0, lane);
+    if (!cur.valid) return;
   }
 
+  // ---- per-lane constants
   const int hh = lane & 15;     // query head within the group (MFMA column)
   const int grp = lane >> 4;    // MFMA row group
   const bool hvalid = hh < a.G;
-  const int h = g * a.G + (hvalid ? hh : 0);
-
-  // ---- q as the B operand of S^T = K . Q^T, d order matching the K loads
-  u32x4 qv[TL::NS];
-  {
-    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + h) * D * 2;
-#pragma unroll
-    for (int s = 0; s < TL::NS; ++s) {
-      int d0;
-      if constexpr (KV == KFP8)
-        d0 = 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
-      else
-        d0 = 32 * s + 8 * grp;
-      u32x4 v = *(const u32x4*)(qrow + d0 * 2);
-      qv[s] = hvalid ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // ---- per-lane byte offsets inside a tile (relative to token 0 of the tile, head g)
-  const int rowstride = a.Hkv * TL::ROWB;    // bytes between consecutive tokens
+  const int hoff = g * a.G + (hvalid ? hh : 0);
+  const int rowstride = a.Hkv * TL::ROWB;               // bytes between consecutive tokens
   int koff[TL::KLD];
 #pragma unroll
   for (int i = 0; i < TL::KLD; ++i) koff[i] = (lane & 15) * rowstride + (4 * i + grp) * 16;
@@ -268,27 +429,39 @@ __global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
     for (int T = 0; T < TL::NT; ++T)
       troff[T] = lds_slot<TL::CPR>(tt, 2 * T + (qq >> 1)) * 16 + (qq & 1) * 8;
   }
-
   const char* kbase = (const char*)a.kc + (size_t)g * TL::ROWB;
   const char* vbase = (const char*)a.vc + (size_t)g * TL::ROWB;
-  const size_t blockbytes = (size_t)BS * rowstride;
+  const size_t blockbytes = (size_t)a.BS * rowstride;
   const int tshift = a.tile_shift;                      // log2(BS / 16)
   const int tmask = (1 << tshift) - 1;
-
-  // Logical block -> physical block id: one scalar load per tile, issued two tiles ahead.
-  // Ids outside [0, num_blocks) are clamped so no access leaves the pool.
-  const int32_t* btrow = a.bt + (size_t)b * a.max_blocks + (t0 >> (tshift + 4));
   const unsigned nbm1 = (unsigned)(a.num_blocks - 1);
-  auto block_of = [&](int tile) -> int {
-    return (int)min((unsigned)btrow[tile >> tshift], nbm1);
+  const int tile_span = 15 * rowstride + TL::ROWB;
+
+  // q of sequence b as the B operand of S^T = K . Q^T, d order matching the K loads
+  auto load_q = [&](int b, u32x4* qv) {
+    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hoff) * D * 2;
+#pragma unroll
+    for (int s = 0; s < TL::NS; ++s) {
+      int d0;
+      if constexpr (KV == KFP8)
+        d0 = 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
+      else
+        d0 = 32 * s + 8 * grp;
+      const u32x4 v = *(const u32x4*)(qrow + d0 * 2);
+      qv[s] = hvalid ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  auto tile_ptr_off = [&](int id, int tile) -> size_t {
-    return (size_t)id * blockbytes + (size_t)(tile & tmask) * 16 * rowstride;
+  // 64 consecutive block ids of sequence b starting at logical block 64*c, one per lane.
+  auto load_window = [&](int b, int c) -> int {
+    const int j = c * 64 + lane;
+    return j < a.max_blocks ? a.bt[(size_t)b * a.max_blocks + j] : 0;
   };
+  auto chunk_of = [&](int tile) -> int { return (tile >> tshift) >> 6; };
   // Raw buffer loads: the descriptor base is the tile's first row (scalar), the lane offsets
   // are fixed VGPRs, and the descriptor's range covers exactly the tile's rows of head g.
-  const int tile_span = 15 * rowstride + TL::ROWB;
-  auto load_tile = [&](size_t off, u32x4* kd, u32x4* vd) {
+  // Block ids outside [0, num_blocks) are clamped so no access leaves the pool.
+  auto load_tile = [&](unsigned id, int tile, u32x4* kd, u32x4* vd) {
+    const size_t off = (size_t)min(id, nbm1) * blockbytes + (size_t)(tile & tmask) * 16 * rowstride;
     const __amdgpu_buffer_rsrc_t kres =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, tile_span, kBufWord3);
     const __amdgpu_buffer_rsrc_t vres =
@@ -301,15 +474,20 @@ __global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
       vd[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff[r], 0, 0));
   };
 
+  // ---- softmax / accumulator state of the current segment
   f32x4 acc[TL::NT];
+  float m, lsum;
+  auto reset = [&]() {
 #pragma unroll
-  for (int T = 0; T < TL::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-  float lsum = 0.f;
+    for (int T = 0; T < TL::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    lsum = 0.f;
+  };
+  reset();
 
-  // One 16-token tile: scores, online softmax, V^T.P^T accumulation.
-  auto compute = [&](int it, const u32x4* kr, const u32x4* vr) {
-    // -- scores S^T = K . Q^T
+  // First half of a tile: scores S^T = K . Q^T and the V tile into LDS.  After it the tile's
+  // registers are free, so the next tile's loads can land in them.
+  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4* qv) -> f32x4 {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < TL::NS; ++st) {
@@ -323,8 +501,6 @@ __global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
       }
       s = mfma_16x16x32<BF>(kop, qv[st], s);
     }
-
-    // -- V tile -> LDS (16-bit, swizzled)
 #pragma unroll
     for (int r = 0; r < TL::VLD; ++r) {
       if constexpr (KV == KFP8) {
@@ -336,12 +512,16 @@ __global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
         *(u32x4*)(vtile + vslot[r]) = vr[r];
       }
     }
+    return s;
+  };
 
-    // -- online softmax (exp2 domain); tokens >= t1 are selected out
-    const int tbase = t0 + (it << 4) + 4 * grp;
+  // Second half: online softmax (exp2 domain) and O^T += V^T . P^T.  Tokens >= n are
+  // selected out of the scores and their V rows are zeroed (stale bytes may be NaN).
+  auto part2 = [&](int tile, int n, f32x4 s) {
+    const int tbase = (tile << 4) + 4 * grp;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (tbase + e < t1) ? s[e] * a.c2 : -INFINITY;
+    for (int e = 0; e < 4; ++e) x[e] = (tbase + e < n) ? s[e] * a.c2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, xor_lanes(mx, 16));
     mx = fmaxf(mx, xor_lanes(mx, 32));
@@ -360,12 +540,10 @@ __global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
       lsum += from16<BF>(ph[e]);
     }
     const u32x2 pop = {pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
-
-    // -- O^T += V^T . P^T; V rows of tokens >= t1 are zeroed (stale bytes may be NaN)
     unsigned vm0 = 0xffffffffu, vm1 = 0xffffffffu;
-    if (t1 - (t0 + (it << 4)) < 16) {
-      vm0 = ((tbase + 0 < t1) ? 0x0000ffffu : 0u) | ((tbase + 1 < t1) ? 0xffff0000u : 0u);
-      vm1 = ((tbase + 2 < t1) ? 0x0000ffffu : 0u) | ((tbase + 3 < t1) ? 0xffff0000u : 0u);
+    if (n - (tile << 4) < 16) {
+      vm0 = ((tbase + 0 < n) ? 0x0000ffffu : 0u) | ((tbase + 1 < n) ? 0xffff0000u : 0u);
+      vm1 = ((tbase + 2 < n) ? 0x0000ffffu : 0u) | ((tbase + 3 < n) ? 0xffff0000u : 0u);
     }
 #pragma unroll
     for (int T = 0; T < TL::NT; ++T) {
@@ -377,80 +555,174 @@ __global__ __launch_bounds__(64) void pa_decode_kernel(DecodeParams a) {
     }
   };
 
-  const int ntiles = (t1 - t0 + 15) >> 4;
-  if (ntiles > 0) {
-    // Ping-pong over two register sets; the tile after the last is the last one again
-    // (an L2 hit), so every prefetch is unconditional and waits stay in program order.
-    const int last = ntiles - 1;
-    u32x4 kA[TL::KLD], vA[TL::VLD], kB[TL::KLD], vB[TL::VLD];
-    int idA = block_of(0);
-    load_tile(tile_ptr_off(idA, 0), kA, vA);
-    int idB = block_of(min(1, last));
-    int it = 0;
-    for (;;) {
-      load_tile(tile_ptr_off(idB, min(it + 1, last)), kB, vB);
-      idA = block_of(min(it + 2, last));
-      compute(it, kA, vA);
-      if (++it > last) break;
-      load_tile(tile_ptr_off(idA, min(it + 1, last)), kA, vA);
-      idB = block_of(min(it + 2, last));
-      compute(it, kB, vB);
-      if (++it > last) break;
+  // Total sum over the 4 row groups, normalise, store the row or the partial.
+  auto finalize = [&](const Seg& sg) {
+    float l = lsum;
+    l += xor_lanes(l, 16);
+    l += xor_lanes(l, 32);
+    if (!hvalid) return;
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    if (a.mode == MODE_SINGLE) {
+      unsigned short* orow = (unsigned short*)a.out + ((size_t)sg.b * a.Hq + hoff) * D;
+#pragma unroll
+      for (int T = 0; T < TL::NT; ++T) {
+        u32x2 wv;
+        wv.x = pack2(f32_to_16<BF>(acc[T][0] * inv), f32_to_16<BF>(acc[T][1] * inv));
+        wv.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
+        *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
+      }
+    } else if (sg.slot >= 0 && sg.slot < a.Pslots) {
+      const size_t prow = ((size_t)sg.b * a.Hq + hoff) * a.Pslots + sg.slot;
+      float* orow = a.tmp_out + prow * D;
+#pragma unroll
+      for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
+      if (grp == 0) {
+        a.max_logits[prow] = m * kLn2;
+        a.exp_sums[prow] = l;
+      }
     }
+  };
+
+  if (cur.thi <= cur.tlo) {                             // single pass, empty context: zeros
+    finalize(cur);
+    return;
   }
 
-  // ---- finish: total sum over the 4 row groups, normalise, store
-  lsum += xor_lanes(lsum, 16);
-  lsum += xor_lanes(lsum, 32);
-  if (!hvalid) return;
-  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+  // ---- prologue: q of this and the next segment, the first two windows of block ids,
+  // the first tile
+  Seg nxt = src.next(cur, lane);
+  u32x4 qc[TL::NS], qn[TL::NS];
+  load_q(cur.b, qc);
+  if (nxt.valid) load_q(nxt.b, qn);
+  int w0b = cur.b, w0c = chunk_of(cur.tlo);             // window in btv0
+  int btv0 = load_window(w0b, w0c);
+  Seg ws = cur;                                         // window iterator: segment, chunk
+  int wc = w0c;
+  SegSource wsrc = src;                                 // its own table (it runs ahead)
+  auto next_window = [&]() -> bool {                    // advance (ws, wc) in stream order
+    if (chunk_of(ws.thi - 1) > wc) {
+      ++wc;
+      return true;
+    }
+    ws = wsrc.next(ws, lane);
+    if (!ws.valid) return false;
+    wc = chunk_of(ws.tlo);
+    return true;
+  };
+  bool w1ok = next_window();
+  int w1b = ws.b, w1c = wc;                             // window in btv1
+  int btv1 = w1ok ? load_window(w1b, w1c) : 0;
 
-  if (a.PS == 0) {
-    unsigned short* orow = (unsigned short*)a.out + ((size_t)b * a.Hq + h) * D;
-#pragma unroll
-    for (int T = 0; T < TL::NT; ++T) {
-      u32x2 w;
-      w.x = pack2(f32_to_16<BF>(acc[T][0] * inv), f32_to_16<BF>(acc[T][1] * inv));
-      w.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
-      *(u32x2*)(orow + 16 * T + 4 * grp) = w;
+  int tile = cur.tlo;
+  u32x4 kr[TL::KLD], vr[TL::VLD];
+  load_tile((unsigned)__builtin_amdgcn_readlane(btv0, (tile >> tshift) - w0c * 64), tile, kr, vr);
+
+  for (;;) {
+    const f32x4 sc = part1(kr, vr, qc);
+    __builtin_amdgcn_sched_barrier(0);
+    // position of the next tile in the stream (the current one again past the end)
+    const bool seg_end = tile + 1 >= cur.thi;
+    int nb = cur.b, ntile = tile;
+    if (!seg_end) {
+      ntile = tile + 1;
+    } else if (nxt.valid) {
+      nb = nxt.b;
+      ntile = nxt.tlo;
     }
-  } else {
-    const size_t prow = ((size_t)b * a.Hq + h) * a.Pmax + p;
-    float* orow = a.tmp_out + prow * D;
-#pragma unroll
-    for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
-    if (grp == 0) {
-      a.max_logits[prow] = m * kLn2;
-      a.exp_sums[prow] = lsum;
+    if (!(nb == w0b && chunk_of(ntile) == w0c) && w1ok) {
+      btv0 = btv1;
+      w0b = w1b;
+      w0c = w1c;
+      w1ok = next_window();
+      w1b = ws.b;
+      w1c = wc;
+      if (w1ok) btv1 = load_window(w1b, w1c);
     }
+    load_tile((unsigned)__builtin_amdgcn_readlane(btv0, (ntile >> tshift) - w0c * 64), ntile, kr, vr);
+    __builtin_amdgcn_sched_barrier(0);
+    part2(tile, cur.n, sc);
+    if (!seg_end) {
+      ++tile;
+      continue;
+    }
+    finalize(cur);
+    if (!nxt.valid) break;
+    reset();
+    cur = nxt;
+#pragma unroll
+    for (int s = 0; s < TL::NS; ++s) qc[s] = qn[s];
+    nxt = src.next(cur, lane);
+    if (nxt.valid) load_q(nxt.b, qn);
+    tile = cur.tlo;
   }
 }
 
 // ------------------------------------------------------------------ split-K reduce
 
+// Block-wide sum of two ints over 256 threads.
+__device__ __forceinline__ void block_sum2(int& x, int& y, int* red) {
+  const int tid = threadIdx.x;
+  red[tid] = x;
+  red[256 + tid] = y;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) {
+      red[tid] += red[tid + s];
+      red[256 + tid] += red[256 + tid + s];
+    }
+    __syncthreads();
+  }
+  x = red[0];
+  y = red[256];
+  __syncthreads();
+}
+
+// One workgroup per (head, sequence).  PS > 0: partials of fixed partitions,
+// P = ceil(n / PS).  PS < 0: balanced split over -PS workgroups; P = number of ranges the
+// sequence's tiles fall in (recomputed from the lengths exactly as the decode did).
 template <int D, bool BF>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* tmp_out,
                                                        const float* max_logits,
                                                        const float* exp_sums,
-                                                       const int32_t* lens, int Hq, int Pmax,
-                                                       int PS) {
+                                                       const int32_t* lens, int B, int Hq,
+                                                       int Pslots, int PS, int cap) {
   constexpr int TPR = D / 4;            // threads per output row (4 floats each)
   constexpr int SLOTS = 256 / TPR;      // partitions processed side by side
   __shared__ float red[256];
+  __shared__ int ired[512];
   __shared__ f32x4 part[256];
 
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int n = lens[b];
-  n = n < 0 ? 0 : n;
-  const int P = min((n + PS - 1) / PS, Pmax);
+  n = n < 0 ? 0 : min(n, cap);
+  int P;
+  if (PS > 0) {
+    P = (n + PS - 1) / PS;
+  } else {
+    int total = 0, before = 0;
+    for (int i = tid; i < B; i += 256) {
+      const int t = tiles_of(lens[i], cap);
+      total += t;
+      before += i < b ? t : 0;
+    }
+    block_sum2(total, before, ired);
+    const int nt = tiles_of(n, cap);
+    if (nt == 0) {
+      P = 0;
+    } else {
+      const int Weff = balanced_weff(total, -PS);
+      P = owner_of(before + nt - 1, total, Weff) - owner_of(before, total, Weff) + 1;
+    }
+  }
+  P = min(P, Pslots);
   const size_t row = (size_t)b * Hq + h;
   unsigned short* orow = (unsigned short*)out + row * D;
   if (P == 0) {
     if (tid < TPR) *(u32x2*)(orow + 4 * tid) = u32x2{0u, 0u};
     return;
   }
-  const float* ml = max_logits + row * Pmax;
-  const float* es = exp_sums + row * Pmax;
+  const float* ml = max_logits + row * Pslots;
+  const float* es = exp_sums + row * Pslots;
 
   float mloc = -INFINITY;
   for (int q = tid; q < P; q += 256) mloc = fmaxf(mloc, ml[q]);
@@ -477,7 +749,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int q = slot; q < P; q += SLOTS) {
     const float w = es[q] * __builtin_amdgcn_exp2f((ml[q] - M) * kLog2e);
-    acc += w * *(const f32x4*)(tmp_out + (row * Pmax + q) * D + 4 * dc);
+    acc += w * *(const f32x4*)(tmp_out + (row * Pslots + q) * D + 4 * dc);
   }
   part[tid] = acc;
   __syncthreads();
@@ -554,14 +826,42 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
-int pmax_of(int max_context_len, int partition_size) {
-  return partition_size > 0 ? (max_context_len + partition_size - 1) / partition_size : 0;
+// Partial slots per (sequence, head): fixed partitions need ceil(max_len / PS); a balanced
+// split gives every workgroup >= kMinChunkTiles tiles, so a sequence meets at most
+// ceil(tiles / kMinChunkTiles) + 1 ranges.
+int slots_of(int max_context_len, int partition_size) {
+  if (partition_size > 0) return (max_context_len + partition_size - 1) / partition_size;
+  if (partition_size < 0) {
+    const int tiles = (max_context_len + 15) / 16;
+    return tiles == 0 ? 0 : (tiles + kMinChunkTiles - 1) / kMinChunkTiles + 1;
+  }
+  return 0;
+}
+
+int waves_per_group(int Hkv) { return Hkv < kMaxWaves ? Hkv : kMaxWaves; }
+int head_groups(int Hkv) { return (Hkv + kMaxWaves - 1) / kMaxWaves; }
+
+template <int D, int KV, bool BF>
+void launch_decode(const DecodeParams& p, hipStream_t st) {
+  const int HG = head_groups(p.Hkv);
+  dim3 grid;
+  if (p.mode == MODE_SINGLE) grid = dim3(p.B, HG);
+  else if (p.mode == MODE_FIXED) grid = dim3(p.Pslots, HG, p.B);
+  else grid = dim3(p.W, HG);
+  const int nw = waves_per_group(p.Hkv);
+  const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
+  hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF>), grid, dim3(64 * nw), lds, st, p);
 }
 
 template <int D, int KV, bool BF>
-void launch_decode(const DecodeParams& p, int B, hipStream_t st) {
-  dim3 grid(p.Hkv, p.PS > 0 ? p.Pmax : 1, B);
-  hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF>), grid, dim3(64), 0, st, p);
+int occupancy_blocks(int Hkv) {
+  int nb = 0;
+  const int nw = waves_per_group(Hkv);
+  const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)pa_decode_kernel<D, KV, BF>, 64 * nw,
+                                                   lds) != hipSuccess)
+    return 0;
+  return nb;
 }
 
 }  // namespace
@@ -584,12 +884,35 @@ const char* pkv_status_string(int status) {
   }
 }
 
+int paged_attn_partial_slots(int max_context_len, int partition_size) {
+  if (max_context_len <= 0) return 0;
+  return slots_of(max_context_len, partition_size);
+}
+
 size_t paged_attn_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
                                   int partition_size) {
-  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+  if (partition_size == 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
     return 0;
-  const size_t P = (size_t)pmax_of(max_context_len, partition_size);
+  const size_t P = (size_t)slots_of(max_context_len, partition_size);
   return (size_t)num_seqs * num_heads * P * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+int paged_attn_balanced_split(int num_kv_heads, int head_dim, int q_dtype, int kv_dtype) {
+  if (num_kv_heads <= 0 || num_kv_heads > 16 || (head_dim != 64 && head_dim != 128)) return 0;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  const bool bf = q_dtype == PKV_BF16, f8 = kv_dtype == PKV_FP8_E4M3;
+  int nb;
+  if (head_dim == 128)
+    nb = f8 ? (bf ? occupancy_blocks<128, KFP8, true>(num_kv_heads) : occupancy_blocks<128, KFP8, false>(num_kv_heads))
+            : (bf ? occupancy_blocks<128, KBF16, true>(num_kv_heads) : occupancy_blocks<128, KF16, false>(num_kv_heads));
+  else
+    nb = f8 ? (bf ? occupancy_blocks<64, KFP8, true>(num_kv_heads) : occupancy_blocks<64, KFP8, false>(num_kv_heads))
+            : (bf ? occupancy_blocks<64, KBF16, true>(num_kv_heads) : occupancy_blocks<64, KF16, false>(num_kv_heads));
+  if (nb <= 0) nb = 1;
+  const int w = prop.multiProcessorCount * nb / head_groups(num_kv_heads);
+  return -(w > 0 ? w : 1);
 }
 
 int paged_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -644,9 +967,10 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
                       float v_scale, int max_context_len, int partition_size, float* tmp_out,
                       float* max_logits, float* exp_sums, void* stream) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks < 0 ||
-      max_context_len < 0 || partition_size < 0)
+      max_context_len < 0 || partition_size < -(1 << 20))
     return PKV_ERR_SHAPE;
-  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16) return PKV_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16 || num_kv_heads > 16)
+    return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_SHAPE;
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0) return PKV_ERR_SHAPE;
   if (partition_size > 0 && (partition_size % block_size != 0)) return PKV_ERR_SHAPE;
@@ -660,15 +984,16 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   if (!query || !key_cache || !value_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
   if (num_blocks == 0 || max_blocks == 0) return PKV_ERR_SHAPE;
   if (partition_size == 0 && !out) return PKV_ERR_NULL;
-  if (partition_size > 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
+  if (partition_size != 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
   if (!aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || (out && !aligned(out, 16)) ||
       (tmp_out && !aligned(tmp_out, 16)) || (max_logits && !aligned(max_logits, 4)) ||
       (exp_sums && !aligned(exp_sums, 4)))
     return PKV_ERR_ALIGN;
-  const int Pmax = pmax_of(max_context_len, partition_size);
-  if (partition_size > 0 && Pmax == 0) return PKV_OK;   // every context is empty
-  if (partition_size > 0 && Pmax > 65535) return PKV_ERR_SHAPE;
+  const int Pslots = slots_of(max_context_len, partition_size);
+  if (partition_size != 0 && Pslots == 0) return PKV_OK;   // every context is empty
+  if (partition_size > 0 && Pslots > 65535) return PKV_ERR_SHAPE;
+  if ((long long)num_seqs * ((max_context_len + 15) / 16) >= (1LL << 31)) return PKV_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
 
   if (check_mode()) {
@@ -687,6 +1012,11 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   }
 
   DecodeParams p;
+  p.B = num_seqs;
+  p.mode = partition_size == 0 ? MODE_SINGLE : (partition_size > 0 ? MODE_FIXED : MODE_BALANCED);
+  p.W = partition_size < 0 ? -partition_size : 0;
+  p.cap = (int)std::min<long long>(max_context_len, (long long)max_blocks * block_size);
+  p.Pslots = Pslots;
   p.out = out;
   p.q = query;
   p.kc = key_cache;
@@ -703,7 +1033,6 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   p.BS = block_size;
   p.num_blocks = num_blocks;
   p.PS = partition_size;
-  p.Pmax = Pmax;
   p.tile_shift = __builtin_ctz((unsigned)block_size) - 4;
   p.c2 = scale * k_scale * kLog2e;
   p.v_scale = v_scale;
@@ -711,11 +1040,11 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   const bool bf = q_dtype == PKV_BF16;
   const bool f8 = kv_dtype == PKV_FP8_E4M3;
   if (head_dim == 128) {
-    if (f8) { if (bf) launch_decode<128, KFP8, true>(p, num_seqs, st); else launch_decode<128, KFP8, false>(p, num_seqs, st); }
-    else    { if (bf) launch_decode<128, KBF16, true>(p, num_seqs, st); else launch_decode<128, KF16, false>(p, num_seqs, st); }
+    if (f8) { if (bf) launch_decode<128, KFP8, true>(p, st); else launch_decode<128, KFP8, false>(p, st); }
+    else    { if (bf) launch_decode<128, KBF16, true>(p, st); else launch_decode<128, KF16, false>(p, st); }
   } else {
-    if (f8) { if (bf) launch_decode<64, KFP8, true>(p, num_seqs, st); else launch_decode<64, KFP8, false>(p, num_seqs, st); }
-    else    { if (bf) launch_decode<64, KBF16, true>(p, num_seqs, st); else launch_decode<64, KF16, false>(p, num_seqs, st); }
+    if (f8) { if (bf) launch_decode<64, KFP8, true>(p, st); else launch_decode<64, KFP8, false>(p, st); }
+    else    { if (bf) launch_decode<64, KBF16, true>(p, st); else launch_decode<64, KF16, false>(p, st); }
   }
   return launch_status();
 }
@@ -723,16 +1052,18 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                       int max_context_len, int partition_size, int out_dtype, void* stream) {
-  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size <= 0) return PKV_ERR_SHAPE;
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size == 0 ||
+      partition_size < -(1 << 20))
+    return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_SHAPE;
   if (out_dtype != PKV_F16 && out_dtype != PKV_BF16) return PKV_ERR_DTYPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !context_lens) return PKV_ERR_NULL;
-  const int Pmax = pmax_of(max_context_len, partition_size);
-  if (Pmax > 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
+  const int Pslots = slots_of(max_context_len, partition_size);
+  if (Pslots > 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
   if (!aligned(out, 16) || (tmp_out && !aligned(tmp_out, 16)) || !aligned(context_lens, 4))
     return PKV_ERR_ALIGN;
-  if (Pmax > 65535) return PKV_ERR_SHAPE;
+  if (Pslots > 65535) return PKV_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
   if (check_mode()) {
     std::vector<int32_t> lens;
@@ -741,14 +1072,14 @@ int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, 
       if (n < 0 || n > max_context_len) return PKV_ERR_CHECK;
   }
   dim3 grid(num_heads, num_seqs), block(256);
-  const int Pm = Pmax > 0 ? Pmax : 1;
+  const int Pm = Pslots > 0 ? Pslots : 1;
   const bool bf = out_dtype == PKV_BF16;
   if (head_dim == 128) {
-    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
-    else    hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
+    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
+    else    hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
   } else {
-    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
-    else    hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_heads, Pm, partition_size);
+    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
+    else    hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
   }
   return launch_status();
 }

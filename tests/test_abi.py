@@ -30,7 +30,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce",
-                          "paged_attn_workspace_bytes", "pkv_status_string"}
+                          "paged_attn_workspace_bytes", "paged_attn_partial_slots",
+                          "paged_attn_balanced_split", "pkv_status_string"}
     L = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -48,6 +49,13 @@ def test_workspace_bytes():
     assert L.paged_attn_workspace_bytes(64, 32, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
     assert L.paged_attn_workspace_bytes(8, 32, 128, 131072, 512) == 8 * 32 * 256 * 130 * 4
     assert L.paged_attn_workspace_bytes(64, 32, 128, 4096, 0) == 0
+    # balanced split: a workgroup gets >= 8 tiles, so a sequence of T tiles meets at most
+    # ceil(T / 8) + 1 ranges
+    assert L.paged_attn_partial_slots(4096, -512) == 256 // 8 + 1
+    assert L.paged_attn_partial_slots(4097, -512) == -(-257 // 8) + 1
+    assert L.paged_attn_partial_slots(1, -3) == 2
+    assert L.paged_attn_partial_slots(0, -3) == 0
+    assert L.paged_attn_workspace_bytes(64, 32, 128, 4096, -512) == 64 * 32 * 33 * 130 * 4
 
 
 def _decode(**kw):
@@ -73,6 +81,8 @@ def _decode(**kw):
     (dict(bt=None), E_NULL),
     (dict(out=None), E_NULL),                  # single pass needs out
     (dict(PS=64), E_WS),                       # split-K needs the partial buffers
+    (dict(PS=-512), E_WS),                     # so does the balanced split
+    (dict(PS=-(1 << 21)), E_SHAPE),
     (dict(q=MIS), E_ALIGN),
     (dict(kc=MIS), E_ALIGN),
     (dict(B=-1), E_SHAPE),

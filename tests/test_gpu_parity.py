@@ -34,12 +34,21 @@ def test_full_write_bitexact(name):
     assert torch.equal(vc.cpu().view(torch.uint8).flatten(), vc_ref.view(torch.uint8).flatten())
 
 
-@pytest.mark.parametrize("name,mode", [(n, m) for n in I.CONFIG_ORDER for m in ("split", "single")])
+def _partition(w, mode):
+    if mode == "split":
+        return w.cfg.partition_size
+    if mode == "balanced":
+        return pk.balanced_split(w.cfg.Hkv, w.cfg.D, I.DTYPES[w.cfg.q_dtype],
+                                 torch.uint8 if w.cfg.kv_dtype == "fp8" else I.DTYPES[w.cfg.kv_dtype])
+    return 0
+
+
+@pytest.mark.parametrize("name,mode", [(n, m) for n in I.CONFIG_ORDER for m in ("balanced", "split", "single")])
 def test_full_decode_parity(name, mode):
     _say(f"[decode] {name} {mode}")
     w, _, _, ref = full_case(name)
     kc, vc = gpu_pools(w)
-    PS = w.cfg.partition_size if mode == "split" else 0
+    PS = _partition(w, mode)
     got = gpu_decode(w, kc, vc, PS, max_context_len=w.cfg.max_len)
     err = max_err(got, ref)
     _say(f"    max-abs err {err:.3e} (tol {tolerance(w.cfg)})")
@@ -73,7 +82,7 @@ def test_stale_nan_slots_do_not_leak(case):
     nan = 0x7F if w.cfg.kv_dtype == "fp8" else float("nan")
     for c in (kc, vc):
         c.view(-1, *c.shape[2:])[stale] = nan
-    for PS in (w.cfg.partition_size, 0):
+    for PS in (w.cfg.partition_size, 0, -64):
         got = gpu_decode(w, kc, vc, PS)
         assert max_err(got, ref) <= tolerance(w.cfg)
         if PS == w.cfg.partition_size:
@@ -93,13 +102,33 @@ def test_deterministic_and_block_permutation_invariant(case):
     kc2, vc2 = gpu_pools(w2)
     c = gpu_decode(w2, kc2, vc2, w.cfg.partition_size)
     assert np.array_equal(a, c)
+    d = gpu_decode(w, kc, vc, -64)
+    e = gpu_decode(w2, kc2, vc2, -64)
+    assert np.array_equal(d, e)
+
+
+@pytest.mark.parametrize("W", [1, 3, 37, 512, 100000])
+def test_balanced_split_any_workgroup_count(W):
+    """Balanced schedules cut sequences at arbitrary tile boundaries; every W must give the
+    oracle's answer, including empty, one-token and single-tile sequences."""
+    _say(f"[balanced] W={W}")
+    cfg = I.Config("bal", 33, B=11, Hq=16, Hkv=4, D=128, block_size=32, q_dtype="bf16", kv_dtype="bf16",
+                   lens=("uniform", 1, 1), pool=("factor", 1.25), max_len=3000, partition_size=512)
+    lens = [0, 1, 16, 17, 2999, 512, 0, 33, 1500, 7, 3000]
+    w = I.permute_blocks(I.dense_workload(cfg, lens, seed=5), seed=6)
+    kc_ref, vc_ref = oracle_pools(w)
+    ref = oracle_decode(w, kc_ref, vc_ref)
+    kc, vc = gpu_pools(w)
+    got = gpu_decode(w, kc, vc, -W, max_context_len=3000)
+    assert max_err(got, ref) <= 1e-2
+    assert np.all(got[0] == 0) and np.all(got[6] == 0)
 
 
 def test_shared_prefix_equals_private_copies_on_gpu():
     _say("[cow] shared_prefix")
     w = _small("shared_prefix", B=16, len_div=2)
     w2 = I.unshare_prefix(w)
-    for PS in (512, 0):
+    for PS in (512, 0, -200):
         kc, vc = gpu_pools(w)
         a = gpu_decode(w, kc, vc, PS)
         kc2, vc2 = gpu_pools(w2)
@@ -185,7 +214,7 @@ def test_needles_at_partition_boundaries():
         vview[slot, 0] = torch.linspace(-2, 2, 128).to(torch.bfloat16)
         w.slot_mapping[:] = -1                     # no write this step
         kc, vc = gpu_pools(w)
-        for PS in (512, 0):
+        for PS in (512, 0, -3):
             got = gpu_decode(w, kc, vc, PS)
             want = vview[slot, 0].float().numpy()
             assert np.max(np.abs(got[0] - want[None, :])) <= 1e-2, (pos, PS)
@@ -212,7 +241,7 @@ def test_partition_indicator_exact_weights():
     sizes = np.minimum(PS, n - PS * np.arange(nparts))
     want = float((a * sizes).sum() / n)
     kc, vc = gpu_pools(w)
-    for P in (PS, 0):
+    for P in (PS, 0, -7, -1000):
         got = gpu_decode(w, kc, vc, P)
         assert np.max(np.abs(got - want)) <= 2e-3 + abs(want) * 2 ** -8, P
 
@@ -277,7 +306,7 @@ def test_shapes_and_ragged_lengths(shape):
     ref = oracle_decode(w, kc_ref, vc_ref)
     kc, vc = gpu_pools(w)
     assert torch.equal(kc.cpu().view(torch.uint8).flatten(), kc_ref.view(torch.uint8).flatten())
-    for PS in (0, 256, max(BS, 64) if BS <= 64 else BS):
+    for PS in (0, 256, max(BS, 64) if BS <= 64 else BS, -5, -300):
         got = gpu_decode(w, kc, vc, PS, max_context_len=2048)
         assert max_err(got, ref) <= tolerance(cfg), PS
 
@@ -291,7 +320,7 @@ def test_empty_and_full_length_sequences():
     kc_ref, vc_ref = oracle_pools(w)
     ref = oracle_decode(w, kc_ref, vc_ref)
     kc, vc = gpu_pools(w)
-    for PS in (128, 0):
+    for PS in (128, 0, -2):
         got = gpu_decode(w, kc, vc, PS, max_context_len=1024)
         assert max_err(got, ref) <= 1e-2
         assert np.all(got[0] == 0) and np.all(got[2] == 0)
