@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from HIP graphs (one per pool copy)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only copy a buffer of this size 5 times (reference for HBM traffic counters)")
     return ap.parse_args()
@@ -184,6 +186,25 @@ def main():
 
     ms_per_step = 1e3 * wall / args.steps
 
+    ms_graph = None
+    if args.graph:
+        # capture one step per pool copy; replay them in the same rotation
+        graphs = []
+        cap_stream = torch.cuda.Stream()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        ms_graph = 1e3 * (time.perf_counter() - tg) / args.steps
+
     dec_logical, dec_unique, nb = decode_bytes(w)
     step_bytes_unique = nb["decode_unique"] + nb["write"]
     step_bytes_logical = nb["decode_logical"] + nb["write"]
@@ -213,6 +234,7 @@ def main():
             "num_blocks": NB, "pool_copies_rotated": copies,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "decode_kernel_ms_mean": round(dec_mean_ms, 5),
         "decode_kernel_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(decode_ms, [10, 50, 90])],

@@ -157,6 +157,8 @@ enum { MODE_SINGLE = 0, MODE_FIXED = 1, MODE_BALANCED = 2 };
 constexpr int kMinChunkTiles = 8;
 // Waves (KV heads) per workgroup; grid.y covers further groups of KV heads.
 constexpr int kMaxWaves = 8;
+// Tiles each wave keeps in flight (register sets of K/V rows).
+constexpr int kPrefetch = 1;
 
 struct DecodeParams {
   void* out;
@@ -211,19 +213,27 @@ __device__ __forceinline__ int lds_slot(int t, int c) {
 __device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 __device__ __forceinline__ int tiles_of(int n, int cap) { return (clamp_len(n, cap) + 15) >> 4; }
 
-// Balanced split of the batch's (sequence, tile) stream of N tiles into Weff equal ranges:
-// range w is [w*N/Weff, (w+1)*N/Weff); owner_of(t) is the range holding tile t.
-__device__ __forceinline__ int balanced_weff(long long N, int W) {
-  long long cap = N / kMinChunkTiles;
-  long long w = W < cap ? W : cap;
-  return w < 1 ? 1 : (int)w;
-}
-__device__ __forceinline__ long long range_lo(int w, long long N, int Weff) {
-  return (long long)w * N / Weff;
-}
-__device__ __forceinline__ int owner_of(long long t, long long N, int Weff) {
-  return (int)(((t + 1) * Weff + N - 1) / N) - 1;
-}
+// Balanced split of the batch's (sequence, tile) stream of N tiles into Weff contiguous
+// ranges whose sizes differ by at most one: the first `rem` ranges hold q+1 tiles, the rest
+// q.  Weff is the requested count, lowered so that q >= kMinChunkTiles.  32-bit arithmetic
+// (N < 2^31 is checked on the host).
+struct Split {
+  int N, Weff, q, rem;
+  Split() = default;
+  __device__ __forceinline__ Split(int n_tiles, int W) {
+    N = n_tiles;
+    const int cap = N / kMinChunkTiles;
+    Weff = W < cap ? W : cap;
+    if (Weff < 1) Weff = 1;
+    q = N / Weff;
+    rem = N - q * Weff;
+  }
+  __device__ __forceinline__ int lo(int w) const { return w * q + (w < rem ? w : rem); }
+  __device__ __forceinline__ int owner(int t) const {   // the range holding tile t
+    const int big = rem * (q + 1);
+    return t < big ? t / (q + 1) : rem + (t - big) / q;
+  }
+};
 
 // A segment: tiles [tlo, thi) of sequence b (n tokens), written to partial `slot` (or, for
 // slot < 0, as the final row).  All fields are wave-uniform.
@@ -238,8 +248,9 @@ struct Seg {
 // sequence b0+k), so moving from one segment to the next is register work only; a workgroup
 // whose range runs past b0+63 refills the table.
 struct SegSource {
-  int mode, B, cap, w, Weff;
-  long long N, lo, hi;
+  int mode, B, cap, w;
+  Split split;
+  long long lo, hi;
   const int32_t* lens;
   int b0;               // first sequence of the table
   long long base;       // global index of sequence b0's first tile
@@ -279,7 +290,7 @@ struct SegSource {
     const long long e = hi < s.start + nt ? hi : s.start + nt;
     s.tlo = (int)(a - s.start);
     s.thi = (int)(e - s.start);
-    s.slot = w - owner_of(s.start, N, Weff);
+    s.slot = w - split.owner((int)s.start);
     s.valid = true;
     return s;
   }
@@ -315,7 +326,7 @@ struct SegSource {
 // tile's loads go out while the current tile is computed, also across segment boundaries,
 // and the next segment's q and the next 64-entry window of block ids are loaded one segment
 // (one window) ahead, so a segment switch costs no memory round trip.
-template <int D, int KV, bool BF>
+template <int D, int KV, bool BF, int MODE>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_decode_kernel(DecodeParams a) {
   using TL = Tile<D, KV>;
@@ -329,17 +340,16 @@ void pa_decode_kernel(DecodeParams a) {
 
   // ---- the workgroup's segments
   SegSource src;
-  src.mode = a.mode;
+  src.mode = MODE;
   src.B = a.B;
   src.cap = cap;
   src.lens = a.lens;
   src.w = 0;
-  src.Weff = 1;
-  src.N = 1;
+  src.split = Split(1, 1);
   src.lo = 0;
   src.hi = 0;
   Seg cur;
-  if (a.mode == MODE_SINGLE) {
+  if constexpr (MODE == MODE_SINGLE) {
     cur.b = blockIdx.x;
     cur.n = src.len(cur.b);
     cur.tlo = 0;
@@ -347,7 +357,7 @@ void pa_decode_kernel(DecodeParams a) {
     cur.slot = -1;
     cur.start = 0;
     cur.valid = true;
-  } else if (a.mode == MODE_FIXED) {
+  } else if constexpr (MODE == MODE_FIXED) {
     cur.b = blockIdx.z;
     cur.n = src.len(cur.b);
     cur.slot = blockIdx.x;
@@ -357,7 +367,7 @@ void pa_decode_kernel(DecodeParams a) {
     cur.valid = cur.thi > cur.tlo;
     if (!cur.valid) return;
   } else {
-    // equal contiguous ranges of the batch's (sequence, tile) stream
+    // MODE_BALANCED: equal contiguous ranges of the batch's (sequence, tile) stream
     const int B = a.B;
     const int per = (B + 63) >> 6;                      // sequences per lane in the scan
     int run = 0, n_first = 0;
@@ -373,16 +383,15 @@ void pa_decode_kernel(DecodeParams a) {
       const int v = __shfl_up(incl, off, 64);
       if (lane >= off) incl += v;
     }
-    const long long N = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    const int N = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     if (N == 0) return;
-    const int Weff = balanced_weff(N, a.W);
+    const Split split(N, a.W);
     const int w = blockIdx.x;
-    if (w >= Weff) return;
+    if (w >= split.Weff) return;
     src.w = w;
-    src.Weff = Weff;
-    src.N = N;
-    src.lo = range_lo(w, N, Weff);
-    src.hi = range_lo(w + 1, N, Weff);
+    src.split = split;
+    src.lo = split.lo(w);
+    src.hi = split.lo(w + 1);
     if (per == 1) {
       src.fill(0, 0, lane, n_first);                    // the scan already holds every length
     } else {
@@ -562,7 +571,7 @@ void pa_decode_kernel(DecodeParams a) {
     l += xor_lanes(l, 32);
     if (!hvalid) return;
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
-    if (a.mode == MODE_SINGLE) {
+    if constexpr (MODE == MODE_SINGLE) {
       unsigned short* orow = (unsigned short*)a.out + ((size_t)sg.b * a.Hq + hoff) * D;
 #pragma unroll
       for (int T = 0; T < TL::NT; ++T) {
@@ -589,16 +598,24 @@ void pa_decode_kernel(DecodeParams a) {
   }
 
   // ---- prologue: q of this and the next segment, the first two windows of block ids,
-  // the first tile
+  // the first kPrefetch tiles
   Seg nxt = src.next(cur, lane);
   u32x4 qc[TL::NS], qn[TL::NS];
   load_q(cur.b, qc);
   if (nxt.valid) load_q(nxt.b, qn);
-  int w0b = cur.b, w0c = chunk_of(cur.tlo);             // window in btv0
+
+  // Issue iterator: the next tile to load runs kPrefetch tiles ahead of the tile computed.
+  // Block ids come from window btv0 (the issue position's window); btv1 holds the window
+  // after it, loaded one window ahead of use.
+  SegSource isrc = src;                                 // own tables: the iterators run
+  SegSource wsrc = src;                                 // at different positions
+  Seg iseg = cur;
+  int itile = cur.tlo;
+  bool idone = false;
+  int w0b = cur.b, w0c = chunk_of(cur.tlo);
   int btv0 = load_window(w0b, w0c);
   Seg ws = cur;                                         // window iterator: segment, chunk
   int wc = w0c;
-  SegSource wsrc = src;                                 // its own table (it runs ahead)
   auto next_window = [&]() -> bool {                    // advance (ws, wc) in stream order
     if (chunk_of(ws.thi - 1) > wc) {
       ++wc;
@@ -610,26 +627,25 @@ void pa_decode_kernel(DecodeParams a) {
     return true;
   };
   bool w1ok = next_window();
-  int w1b = ws.b, w1c = wc;                             // window in btv1
+  int w1b = ws.b, w1c = wc;
   int btv1 = w1ok ? load_window(w1b, w1c) : 0;
-
-  int tile = cur.tlo;
-  u32x4 kr[TL::KLD], vr[TL::VLD];
-  load_tile((unsigned)__builtin_amdgcn_readlane(btv0, (tile >> tshift) - w0c * 64), tile, kr, vr);
-
-  for (;;) {
-    const f32x4 sc = part1(kr, vr, qc);
-    __builtin_amdgcn_sched_barrier(0);
-    // position of the next tile in the stream (the current one again past the end)
-    const bool seg_end = tile + 1 >= cur.thi;
-    int nb = cur.b, ntile = tile;
-    if (!seg_end) {
-      ntile = tile + 1;
-    } else if (nxt.valid) {
-      nb = nxt.b;
-      ntile = nxt.tlo;
+  // Load the tile at the issue position, then advance it (past the stream's end the last
+  // tile is loaded again: an L2 hit that keeps every load unconditional).
+  auto issue = [&](u32x4* kd, u32x4* vd) {
+    load_tile((unsigned)__builtin_amdgcn_readlane(btv0, (itile >> tshift) - w0c * 64), itile, kd, vd);
+    if (idone) return;
+    if (itile + 1 < iseg.thi) {
+      ++itile;
+    } else {
+      const Seg s2 = isrc.next(iseg, lane);
+      if (!s2.valid) {
+        idone = true;
+        return;
+      }
+      iseg = s2;
+      itile = s2.tlo;
     }
-    if (!(nb == w0b && chunk_of(ntile) == w0c) && w1ok) {
+    if (!(iseg.b == w0b && chunk_of(itile) == w0c) && w1ok) {
       btv0 = btv1;
       w0b = w1b;
       w0c = w1c;
@@ -638,22 +654,40 @@ void pa_decode_kernel(DecodeParams a) {
       w1c = wc;
       if (w1ok) btv1 = load_window(w1b, w1c);
     }
-    load_tile((unsigned)__builtin_amdgcn_readlane(btv0, (ntile >> tshift) - w0c * 64), ntile, kr, vr);
-    __builtin_amdgcn_sched_barrier(0);
-    part2(tile, cur.n, sc);
-    if (!seg_end) {
-      ++tile;
-      continue;
-    }
-    finalize(cur);
-    if (!nxt.valid) break;
-    reset();
-    cur = nxt;
+  };
+
+  u32x4 kr[kPrefetch][TL::KLD], vr[kPrefetch][TL::VLD];
 #pragma unroll
-    for (int s = 0; s < TL::NS; ++s) qc[s] = qn[s];
-    nxt = src.next(cur, lane);
-    if (nxt.valid) load_q(nxt.b, qn);
-    tile = cur.tlo;
+  for (int r = 0; r < kPrefetch; ++r) issue(kr[r], vr[r]);
+
+  int tile = cur.tlo;
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int r = 0; r < kPrefetch; ++r) {
+      if (done) break;
+      const f32x4 sc = part1(kr[r], vr[r], qc);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kr[r], vr[r]);                              // set r is free again
+      __builtin_amdgcn_sched_barrier(0);
+      part2(tile, cur.n, sc);
+      if (tile + 1 < cur.thi) {
+        ++tile;
+        continue;
+      }
+      finalize(cur);
+      if (!nxt.valid) {
+        done = true;
+        break;
+      }
+      reset();
+      cur = nxt;
+#pragma unroll
+      for (int s = 0; s < TL::NS; ++s) qc[s] = qn[s];
+      nxt = src.next(cur, lane);
+      if (nxt.valid) load_q(nxt.b, qn);
+      tile = cur.tlo;
+    }
   }
 }
 
@@ -710,8 +744,8 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
     if (nt == 0) {
       P = 0;
     } else {
-      const int Weff = balanced_weff(total, -PS);
-      P = owner_of(before + nt - 1, total, Weff) - owner_of(before, total, Weff) + 1;
+      const Split split(total, -PS);
+      P = split.owner(before + nt - 1) - split.owner(before) + 1;
     }
   }
   P = min(P, Pslots);
@@ -844,13 +878,15 @@ int head_groups(int Hkv) { return (Hkv + kMaxWaves - 1) / kMaxWaves; }
 template <int D, int KV, bool BF>
 void launch_decode(const DecodeParams& p, hipStream_t st) {
   const int HG = head_groups(p.Hkv);
-  dim3 grid;
-  if (p.mode == MODE_SINGLE) grid = dim3(p.B, HG);
-  else if (p.mode == MODE_FIXED) grid = dim3(p.Pslots, HG, p.B);
-  else grid = dim3(p.W, HG);
   const int nw = waves_per_group(p.Hkv);
   const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
-  hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF>), grid, dim3(64 * nw), lds, st, p);
+  if (p.mode == MODE_SINGLE)
+    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_SINGLE>), dim3(p.B, HG), dim3(64 * nw), lds, st, p);
+  else if (p.mode == MODE_FIXED)
+    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_FIXED>), dim3(p.Pslots, HG, p.B), dim3(64 * nw), lds,
+                       st, p);
+  else
+    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED>), dim3(p.W, HG), dim3(64 * nw), lds, st, p);
 }
 
 template <int D, int KV, bool BF>
@@ -858,8 +894,8 @@ int occupancy_blocks(int Hkv) {
   int nb = 0;
   const int nw = waves_per_group(Hkv);
   const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)pa_decode_kernel<D, KV, BF>, 64 * nw,
-                                                   lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &nb, (const void*)pa_decode_kernel<D, KV, BF, MODE_BALANCED>, 64 * nw, lds) != hipSuccess)
     return 0;
   return nb;
 }
