@@ -67,6 +67,19 @@ def copy_reference(mib):
                       "read_plus_write_gbps": round(2 * mib * 2 ** 20 / dt / 1e9, 1)}), flush=True)
 
 
+def measured_traffic(workload, schedule):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of
+    this workload, or None if there is none or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.json")
+    if schedule != "balanced" or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "paged_kv_cache_224_amd", "csrc", "pagedkv.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return int(rec["decode_traffic_bytes"]) if rec.get("kernel_source_sha256_16") == h else None
+
+
 def decode_bytes(w):
     """Algorithmic bytes of one decode launch: KV rows of every (sequence, token) once, q,
     the used block-table entries and the context lengths (logical and unique-block counts)."""
@@ -245,7 +258,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, schedule),
             "kernel": "pa_decode_kernel",
             "bytes_per_launch": dec_unique,
         },
