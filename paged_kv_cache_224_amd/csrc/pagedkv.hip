@@ -145,20 +145,50 @@ __device__ __forceinline__ unsigned e4m3fn_code(float y) {
 
 // ------------------------------------------------------------------ cross-lane helpers
 
-__device__ __forceinline__ float xor_lanes(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// Butterfly partners across the four 16-lane rows, on the VALU (no LDS round trip):
+// permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap pairs the two 32-lane halves.  Both
+// returned halves hold the same two operands, so op(r[0], r[1]) is the pair's combined value
+// in every lane, bit for bit the same in both partners.
+__device__ __forceinline__ float max_rows16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_rows32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_rows16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_rows32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4, 8 inside each 16-lane
+// row, then row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the first
+// half's total into rows 2 and 3 (row_bcast:31).  Lanes without a source add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
 }
 
 // ------------------------------------------------------------------ decode kernel
 
+// Schedules: one workgroup per sequence; fixed token partitions; a balanced split of the
+// batch's tile stream (both split schedules leave partials for paged_attn_reduce).
 enum { MODE_SINGLE = 0, MODE_FIXED = 1, MODE_BALANCED = 2 };
 
 // Balanced split: fewest tiles a workgroup gets (bounds the partial slots per sequence).
 constexpr int kMinChunkTiles = 8;
 // Waves (KV heads) per workgroup; grid.y covers further groups of KV heads.
 constexpr int kMaxWaves = 8;
-// Tiles each wave keeps in flight (register sets of K/V rows).
-constexpr int kPrefetch = 1;
 
 struct DecodeParams {
   void* out;
@@ -266,13 +296,7 @@ struct SegSource {
     base = start;
     n_v = n_lane;
     const int t = (n_v + 15) >> 4;
-    int incl = t;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    st_v = incl - t;
+    st_v = wave_incl_scan(t) - t;
     const long long s0 = start + st_v;
     vmask = __ballot(t > 0 && s0 < hi && s0 + t > lo);
   }
@@ -323,9 +347,10 @@ struct SegSource {
 // One workgroup = up to kMaxWaves waves; wave i handles KV head g = blockIdx.y*kMaxWaves + i,
 // so the waves stream whole blocks ([BS][Hkv][D] is contiguous) together.  Each wave owns one
 // LDS tile and runs one continuous tile pipeline over all segments of its workgroup: the next
-// tile's loads go out while the current tile is computed, also across segment boundaries,
-// and the next segment's q and the next 64-entry window of block ids are loaded one segment
-// (one window) ahead, so a segment switch costs no memory round trip.
+// tile's loads go out while the current tile is computed, also across segment boundaries.
+// Every load result is first read at least one tile after it was issued, and nothing waits
+// on a value right after loading it, so the in-order load counter never drains the tile
+// in flight.
 template <int D, int KV, bool BF, int MODE>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_decode_kernel(DecodeParams a) {
@@ -377,13 +402,8 @@ void pa_decode_kernel(DecodeParams a) {
       if (i == 0) n_first = n;
       run += (n + 15) >> 4;
     }
-    int incl = run;                                     // inclusive scan over lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    const int N = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    const int incl = wave_incl_scan(run);               // inclusive scan over lanes
+    const int N = __builtin_amdgcn_readlane(incl, 63);
     if (N == 0) return;
     const Split split(N, a.W);
     const int w = blockIdx.x;
@@ -399,7 +419,7 @@ void pa_decode_kernel(DecodeParams a) {
       const unsigned long long hit = __ballot(incl > src.lo);
       if (hit == 0) return;                             // unreachable for lo < N
       const int L = __builtin_ctzll(hit);
-      src.fill_load(L * per, __builtin_amdgcn_readfirstlane(__shfl(incl - run, L, 64)), lane);
+      src.fill_load(L * per, __builtin_amdgcn_readlane(incl - run, L), lane);
     }
     cur = src.from_lane(0, lane);
     if (!cur.valid) return;
@@ -446,7 +466,9 @@ void pa_decode_kernel(DecodeParams a) {
   const unsigned nbm1 = (unsigned)(a.num_blocks - 1);
   const int tile_span = 15 * rowstride + TL::ROWB;
 
-  // q of sequence b as the B operand of S^T = K . Q^T, d order matching the K loads
+  // q of sequence b as the B operand of S^T = K . Q^T, d order matching the K loads.  Lanes
+  // of MFMA columns >= G load a valid head of the group: those columns are computed and
+  // dropped, and no select on the loaded value forces a wait right after the loads.
   auto load_q = [&](int b, u32x4* qv) {
     const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hoff) * D * 2;
 #pragma unroll
@@ -456,16 +478,14 @@ void pa_decode_kernel(DecodeParams a) {
         d0 = 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
       else
         d0 = 32 * s + 8 * grp;
-      const u32x4 v = *(const u32x4*)(qrow + d0 * 2);
-      qv[s] = hvalid ? v : u32x4{0u, 0u, 0u, 0u};
+      qv[s] = *(const u32x4*)(qrow + d0 * 2);
     }
   };
-  // 64 consecutive block ids of sequence b starting at logical block 64*c, one per lane.
-  auto load_window = [&](int b, int c) -> int {
-    const int j = c * 64 + lane;
-    return j < a.max_blocks ? a.bt[(size_t)b * a.max_blocks + j] : 0;
+  // Physical block of logical tile `tile` of sequence b (a wave-uniform address; the tile
+  // index is below ceil(n / 16) with n <= max_blocks * BS, so the entry is inside the row).
+  auto load_id = [&](int b, int tile) -> int {
+    return a.bt[(size_t)b * a.max_blocks + (tile >> tshift)];
   };
-  auto chunk_of = [&](int tile) -> int { return (tile >> tshift) >> 6; };
   // Raw buffer loads: the descriptor base is the tile's first row (scalar), the lane offsets
   // are fixed VGPRs, and the descriptor's range covers exactly the tile's rows of head g.
   // Block ids outside [0, num_blocks) are clamped so no access leaves the pool.
@@ -532,8 +552,7 @@ void pa_decode_kernel(DecodeParams a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = (tbase + e < n) ? s[e] * a.c2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, xor_lanes(mx, 16));
-    mx = fmaxf(mx, xor_lanes(mx, 32));
+    mx = max_rows32(max_rows16(mx));
     if (__ballot(mx > m) != 0) {
       const float mn = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -566,28 +585,27 @@ void pa_decode_kernel(DecodeParams a) {
 
   // Total sum over the 4 row groups, normalise, store the row or the partial.
   auto finalize = [&](const Seg& sg) {
-    float l = lsum;
-    l += xor_lanes(l, 16);
-    l += xor_lanes(l, 32);
-    if (!hvalid) return;
+    const float l = sum_rows32(sum_rows16(lsum));
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
-    if constexpr (MODE == MODE_SINGLE) {
-      unsigned short* orow = (unsigned short*)a.out + ((size_t)sg.b * a.Hq + hoff) * D;
+    if (hvalid) {
+      if constexpr (MODE == MODE_SINGLE) {
+        unsigned short* orow = (unsigned short*)a.out + ((size_t)sg.b * a.Hq + hoff) * D;
 #pragma unroll
-      for (int T = 0; T < TL::NT; ++T) {
-        u32x2 wv;
-        wv.x = pack2(f32_to_16<BF>(acc[T][0] * inv), f32_to_16<BF>(acc[T][1] * inv));
-        wv.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
-        *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
-      }
-    } else if (sg.slot >= 0 && sg.slot < a.Pslots) {
-      const size_t prow = ((size_t)sg.b * a.Hq + hoff) * a.Pslots + sg.slot;
-      float* orow = a.tmp_out + prow * D;
+        for (int T = 0; T < TL::NT; ++T) {
+          u32x2 wv;
+          wv.x = pack2(f32_to_16<BF>(acc[T][0] * inv), f32_to_16<BF>(acc[T][1] * inv));
+          wv.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
+          *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
+        }
+      } else if (sg.slot >= 0 && sg.slot < a.Pslots) {
+        const size_t prow = ((size_t)sg.b * a.Hq + hoff) * a.Pslots + sg.slot;
+        float* orow = a.tmp_out + prow * D;
 #pragma unroll
-      for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
-      if (grp == 0) {
-        a.max_logits[prow] = m * kLn2;
-        a.exp_sums[prow] = l;
+        for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
+        if (grp == 0) {
+          a.max_logits[prow] = m * kLn2;
+          a.exp_sums[prow] = l;
+        }
       }
     }
   };
@@ -597,42 +615,23 @@ void pa_decode_kernel(DecodeParams a) {
     return;
   }
 
-  // ---- prologue: q of this and the next segment, the first two windows of block ids,
-  // the first kPrefetch tiles
-  Seg nxt = src.next(cur, lane);
-  u32x4 qc[TL::NS], qn[TL::NS];
+  // ---- prologue: q of the first segment, the first tile's block id and the first tile
+  u32x4 qc[TL::NS];
   load_q(cur.b, qc);
-  if (nxt.valid) load_q(nxt.b, qn);
 
-  // Issue iterator: the next tile to load runs kPrefetch tiles ahead of the tile computed.
-  // Block ids come from window btv0 (the issue position's window); btv1 holds the window
-  // after it, loaded one window ahead of use.
-  SegSource isrc = src;                                 // own tables: the iterators run
-  SegSource wsrc = src;                                 // at different positions
-  Seg iseg = cur;
+  // Issue iterator: (iseg, itile) is the next tile to load; its block id sits in `nid`,
+  // loaded one tile ahead of the tile's own loads, so reading it never waits for loads that
+  // are still in flight.
+  SegSource isrc = src;                                 // own table: the iterators run
+  Seg iseg = cur;                                       // at different positions
   int itile = cur.tlo;
   bool idone = false;
-  int w0b = cur.b, w0c = chunk_of(cur.tlo);
-  int btv0 = load_window(w0b, w0c);
-  Seg ws = cur;                                         // window iterator: segment, chunk
-  int wc = w0c;
-  auto next_window = [&]() -> bool {                    // advance (ws, wc) in stream order
-    if (chunk_of(ws.thi - 1) > wc) {
-      ++wc;
-      return true;
-    }
-    ws = wsrc.next(ws, lane);
-    if (!ws.valid) return false;
-    wc = chunk_of(ws.tlo);
-    return true;
-  };
-  bool w1ok = next_window();
-  int w1b = ws.b, w1c = wc;
-  int btv1 = w1ok ? load_window(w1b, w1c) : 0;
-  // Load the tile at the issue position, then advance it (past the stream's end the last
-  // tile is loaded again: an L2 hit that keeps every load unconditional).
+  int nid = load_id(cur.b, cur.tlo);
+  // Load the tile at the issue position, then advance it and fetch the next block id (past
+  // the stream's end the last tile is loaded again: an L2 hit that keeps every load
+  // unconditional).
   auto issue = [&](u32x4* kd, u32x4* vd) {
-    load_tile((unsigned)__builtin_amdgcn_readlane(btv0, (itile >> tshift) - w0c * 64), itile, kd, vd);
+    load_tile((unsigned)__builtin_amdgcn_readfirstlane(nid), itile, kd, vd);
     if (idone) return;
     if (itile + 1 < iseg.thi) {
       ++itile;
@@ -645,102 +644,68 @@ void pa_decode_kernel(DecodeParams a) {
       iseg = s2;
       itile = s2.tlo;
     }
-    if (!(iseg.b == w0b && chunk_of(itile) == w0c) && w1ok) {
-      btv0 = btv1;
-      w0b = w1b;
-      w0c = w1c;
-      w1ok = next_window();
-      w1b = ws.b;
-      w1c = wc;
-      if (w1ok) btv1 = load_window(w1b, w1c);
-    }
+    nid = load_id(iseg.b, itile);
   };
 
-  u32x4 kr[kPrefetch][TL::KLD], vr[kPrefetch][TL::VLD];
-#pragma unroll
-  for (int r = 0; r < kPrefetch; ++r) issue(kr[r], vr[r]);
+  u32x4 kr[TL::KLD], vr[TL::VLD];
+  issue(kr, vr);
 
   int tile = cur.tlo;
-  bool done = false;
-  while (!done) {
-#pragma unroll
-    for (int r = 0; r < kPrefetch; ++r) {
-      if (done) break;
-      const f32x4 sc = part1(kr[r], vr[r], qc);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(kr[r], vr[r]);                              // set r is free again
-      __builtin_amdgcn_sched_barrier(0);
-      part2(tile, cur.n, sc);
-      if (tile + 1 < cur.thi) {
-        ++tile;
-        continue;
-      }
-      finalize(cur);
-      if (!nxt.valid) {
-        done = true;
-        break;
-      }
-      reset();
-      cur = nxt;
-#pragma unroll
-      for (int s = 0; s < TL::NS; ++s) qc[s] = qn[s];
-      nxt = src.next(cur, lane);
-      if (nxt.valid) load_q(nxt.b, qn);
-      tile = cur.tlo;
+  for (;;) {
+    const f32x4 sc = part1(kr, vr, qc);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kr, vr);                                      // the tile registers are free again
+    __builtin_amdgcn_sched_barrier(0);
+    part2(tile, cur.n, sc);
+    if (tile + 1 < cur.thi) {
+      ++tile;
+      continue;
     }
+    finalize(cur);
+    const Seg nx = src.next(cur, lane);
+    if (!nx.valid) break;
+    // next segment: its q is loaded now and first used after the next tile's loads, which
+    // were issued before it, have landed
+    reset();
+    cur = nx;
+    load_q(cur.b, qc);
+    tile = cur.tlo;
   }
 }
 
 // ------------------------------------------------------------------ split-K reduce
 
-// Block-wide sum of two ints over 256 threads.
-__device__ __forceinline__ void block_sum2(int& x, int& y, int* red) {
-  const int tid = threadIdx.x;
-  red[tid] = x;
-  red[256 + tid] = y;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) {
-      red[tid] += red[tid + s];
-      red[256 + tid] += red[256 + tid + s];
-    }
-    __syncthreads();
-  }
-  x = red[0];
-  y = red[256];
-  __syncthreads();
-}
-
-// One workgroup per (head, sequence).  PS > 0: partials of fixed partitions,
-// P = ceil(n / PS).  PS < 0: balanced split over -PS workgroups; P = number of ranges the
-// sequence's tiles fall in (recomputed from the lengths exactly as the decode did).
+// One wave per output row (sequence b, query head h); four rows per workgroup.  PS > 0:
+// partials of fixed partitions, P = ceil(n / PS).  PS < 0: balanced split over -PS
+// workgroups; P = number of ranges the sequence's tiles fall in, recomputed from the lengths
+// exactly as the decode did.  The merge needs no LDS and no barrier: each lane accumulates
+// D/64 output elements over the partials in slot order.
 template <int D, bool BF>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* tmp_out,
                                                        const float* max_logits,
                                                        const float* exp_sums,
                                                        const int32_t* lens, int B, int Hq,
                                                        int Pslots, int PS, int cap) {
-  constexpr int TPR = D / 4;            // threads per output row (4 floats each)
-  constexpr int SLOTS = 256 / TPR;      // partitions processed side by side
-  __shared__ float red[256];
-  __shared__ int ired[512];
-  __shared__ f32x4 part[256];
-
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  int n = lens[b];
-  n = n < 0 ? 0 : min(n, cap);
+  constexpr int DPL = D / 64;                 // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // b * Hq + h
+  if (row >= B * Hq) return;
+  const int b = row / Hq;
+  const int n = clamp_len(__builtin_amdgcn_readfirstlane(lens[b]), cap);
   int P;
   if (PS > 0) {
     P = (n + PS - 1) / PS;
   } else {
-    int total = 0, before = 0;
-    for (int i = tid; i < B; i += 256) {
-      const int t = tiles_of(lens[i], cap);
+    int total = 0, before = 0;               // tiles of the whole batch, of sequences < b
+    for (int i0 = 0; i0 < B; i0 += 64) {
+      const int i = i0 + lane;
+      const int t = i < B ? tiles_of(lens[i], cap) : 0;
       total += t;
       before += i < b ? t : 0;
     }
-    block_sum2(total, before, ired);
-    const int nt = tiles_of(n, cap);
+    total = __builtin_amdgcn_readlane(wave_incl_scan(total), 63);
+    before = __builtin_amdgcn_readlane(wave_incl_scan(before), 63);
+    const int nt = (n + 15) >> 4;
     if (nt == 0) {
       P = 0;
     } else {
@@ -749,53 +714,57 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
     }
   }
   P = min(P, Pslots);
-  const size_t row = (size_t)b * Hq + h;
-  unsigned short* orow = (unsigned short*)out + row * D;
+  unsigned short* orow = (unsigned short*)out + (size_t)row * D + lane * DPL;
   if (P == 0) {
-    if (tid < TPR) *(u32x2*)(orow + 4 * tid) = u32x2{0u, 0u};
+    if constexpr (DPL == 2)
+      *(unsigned*)orow = 0u;
+    else
+      *orow = 0;
     return;
   }
-  const float* ml = max_logits + row * Pslots;
-  const float* es = exp_sums + row * Pslots;
+  const float* ml = max_logits + (size_t)row * Pslots;
+  const float* es = exp_sums + (size_t)row * Pslots;
+  const float* to = tmp_out + (size_t)row * Pslots * D + lane * DPL;
 
-  float mloc = -INFINITY;
-  for (int q = tid; q < P; q += 256) mloc = fmaxf(mloc, ml[q]);
-  red[tid] = mloc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
+  // Running-maximum merge in slot order: lane p % 64 holds (m_p, l_p); every lane folds the
+  // partials in one by one (the weights are wave-uniform), so the partial rows, maxima and
+  // sums are all requested in the same round trip.
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  float mrun = -INFINITY, wrun = 0.f;
+  for (int p0 = 0; p0 < P; p0 += 64) {
+    const int p = p0 + lane;
+    const float mp = p < P ? ml[p] * kLog2e : -INFINITY;
+    const float lp = p < P ? es[p] : 0.f;
+    const int cnt = min(64, P - p0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float* src = to + (size_t)(p0 + j) * D;
+      float o[DPL];
+      if constexpr (DPL == 2) {
+        const float2 v = *(const float2*)src;
+        o[0] = v.x;
+        o[1] = v.y;
+      } else {
+        o[0] = src[0];
+      }
+      const float mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mp), j));
+      const float lj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), j));
+      const float mn = fmaxf(mrun, mj);
+      const float so = __builtin_amdgcn_exp2f(mrun - mn);
+      const float sn = lj * __builtin_amdgcn_exp2f(mj - mn);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * so + o[i] * sn;
+      wrun = wrun * so + sn;
+      mrun = mn;
+    }
   }
-  const float M = red[0];
-  __syncthreads();
-
-  float wloc = 0.f;
-  for (int q = tid; q < P; q += 256) wloc += es[q] * __builtin_amdgcn_exp2f((ml[q] - M) * kLog2e);
-  red[tid] = wloc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const float W = red[0];
-
-  const int dc = tid % TPR, slot = tid / TPR;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int q = slot; q < P; q += SLOTS) {
-    const float w = es[q] * __builtin_amdgcn_exp2f((ml[q] - M) * kLog2e);
-    acc += w * *(const f32x4*)(tmp_out + (row * Pslots + q) * D + 4 * dc);
-  }
-  part[tid] = acc;
-  __syncthreads();
-  if (slot == 0) {
-    f32x4 t = part[dc];
-    for (int s = 1; s < SLOTS; ++s) t += part[s * TPR + dc];
-    const float inv = 1.0f / W;
-    u32x2 w;
-    w.x = pack2(f32_to_16<BF>(t[0] * inv), f32_to_16<BF>(t[1] * inv));
-    w.y = pack2(f32_to_16<BF>(t[2] * inv), f32_to_16<BF>(t[3] * inv));
-    *(u32x2*)(orow + 4 * dc) = w;
-  }
+  const float inv = 1.0f / wrun;
+  if constexpr (DPL == 2)
+    *(unsigned*)orow = pack2(f32_to_16<BF>(acc[0] * inv), f32_to_16<BF>(acc[1] * inv));
+  else
+    *orow = f32_to_16<BF>(acc[0] * inv);
 }
 
 // ------------------------------------------------------------------ KV write scatter
@@ -1099,7 +1068,7 @@ int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, 
   if (Pslots > 0 && (!tmp_out || !max_logits || !exp_sums)) return PKV_ERR_WORKSPACE;
   if (!aligned(out, 16) || (tmp_out && !aligned(tmp_out, 16)) || !aligned(context_lens, 4))
     return PKV_ERR_ALIGN;
-  if (Pslots > 65535) return PKV_ERR_SHAPE;
+  if (Pslots > 65535 || (long long)num_seqs * num_heads >= (1LL << 31)) return PKV_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
   if (check_mode()) {
     std::vector<int32_t> lens;
@@ -1107,7 +1076,7 @@ int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, 
     for (int n : lens)
       if (n < 0 || n > max_context_len) return PKV_ERR_CHECK;
   }
-  dim3 grid(num_heads, num_seqs), block(256);
+  dim3 grid((unsigned)(((long long)num_seqs * num_heads + 3) / 4)), block(256);
   const int Pm = Pslots > 0 ? Pslots : 1;
   const bool bf = out_dtype == PKV_BF16;
   if (head_dim == 128) {
