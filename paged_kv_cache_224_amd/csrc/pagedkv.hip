@@ -678,16 +678,18 @@ void pa_decode_kernel(DecodeParams a) {
 // One wave per output row (sequence b, query head h); four rows per workgroup.  PS > 0:
 // partials of fixed partitions, P = ceil(n / PS).  PS < 0: balanced split over -PS
 // workgroups; P = number of ranges the sequence's tiles fall in, recomputed from the lengths
-// exactly as the decode did.  The merge needs no LDS and no barrier: each lane accumulates
-// D/64 output elements over the partials in slot order.
+// exactly as the decode did.  No LDS and no barrier: 16-lane row r of the wave folds the
+// partials p = r, r+4, ... into a running (max, weight sum, weighted o) over its D/16 output
+// elements per lane, and the four rows are combined with permlane swaps.
 template <int D, bool BF>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* tmp_out,
                                                        const float* max_logits,
                                                        const float* exp_sums,
                                                        const int32_t* lens, int B, int Hq,
                                                        int Pslots, int PS, int cap) {
-  constexpr int DPL = D / 64;                 // output elements per lane
+  constexpr int DPL = D / 16;                 // output elements per lane (8 or 4)
   const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, l16 = lane & 15;
   const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // b * Hq + h
   if (row >= B * Hq) return;
   const int b = row / Hq;
@@ -714,57 +716,62 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
     }
   }
   P = min(P, Pslots);
-  unsigned short* orow = (unsigned short*)out + (size_t)row * D + lane * DPL;
+  unsigned short* orow = (unsigned short*)out + (size_t)row * D + l16 * DPL;
   if (P == 0) {
-    if constexpr (DPL == 2)
-      *(unsigned*)orow = 0u;
-    else
-      *orow = 0;
+    if (grp == 0) {
+      if constexpr (DPL == 8)
+        *(u32x4*)orow = u32x4{0u, 0u, 0u, 0u};
+      else
+        *(u32x2*)orow = u32x2{0u, 0u};
+    }
     return;
   }
   const float* ml = max_logits + (size_t)row * Pslots;
   const float* es = exp_sums + (size_t)row * Pslots;
-  const float* to = tmp_out + (size_t)row * Pslots * D + lane * DPL;
+  const float* to = tmp_out + (size_t)row * Pslots * D + l16 * DPL;
 
-  // Running-maximum merge in slot order: lane p % 64 holds (m_p, l_p); every lane folds the
-  // partials in one by one (the weights are wave-uniform), so the partial rows, maxima and
-  // sums are all requested in the same round trip.
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   float mrun = -INFINITY, wrun = 0.f;
-  for (int p0 = 0; p0 < P; p0 += 64) {
-    const int p = p0 + lane;
-    const float mp = p < P ? ml[p] * kLog2e : -INFINITY;
-    const float lp = p < P ? es[p] : 0.f;
-    const int cnt = min(64, P - p0);
-#pragma unroll 8
-    for (int j = 0; j < cnt; ++j) {
-      const float* src = to + (size_t)(p0 + j) * D;
-      float o[DPL];
-      if constexpr (DPL == 2) {
-        const float2 v = *(const float2*)src;
-        o[0] = v.x;
-        o[1] = v.y;
-      } else {
-        o[0] = src[0];
-      }
-      const float mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mp), j));
-      const float lj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), j));
-      const float mn = fmaxf(mrun, mj);
-      const float so = __builtin_amdgcn_exp2f(mrun - mn);
-      const float sn = lj * __builtin_amdgcn_exp2f(mj - mn);
+#pragma unroll 4
+  for (int p = grp; p < P; p += 4) {
+    const float mp = ml[p] * kLog2e;
+    const float lp = es[p];
+    float o[DPL];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * so + o[i] * sn;
-      wrun = wrun * so + sn;
-      mrun = mn;
+    for (int i = 0; i < DPL; i += 4) {
+      const f32x4 v = *(const f32x4*)(to + (size_t)p * D + i);
+      o[i] = v[0];
+      o[i + 1] = v[1];
+      o[i + 2] = v[2];
+      o[i + 3] = v[3];
     }
+    const float mn = fmaxf(mrun, mp);
+    const float so = __builtin_amdgcn_exp2f(mrun - mn);
+    const float sn = lp * __builtin_amdgcn_exp2f(mp - mn);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * so + o[i] * sn;
+    wrun = wrun * so + sn;
+    mrun = mn;
   }
-  const float inv = 1.0f / wrun;
-  if constexpr (DPL == 2)
-    *(unsigned*)orow = pack2(f32_to_16<BF>(acc[0] * inv), f32_to_16<BF>(acc[1] * inv));
-  else
-    *orow = f32_to_16<BF>(acc[0] * inv);
+  // combine the four rows: rescale each to the common maximum (a row without partials has
+  // mrun = -inf and weight 0), then sum across rows
+  const float M = max_rows32(max_rows16(mrun));
+  const float sg = __builtin_amdgcn_exp2f(mrun - M);
+  const float inv = 1.0f / sum_rows32(sum_rows16(wrun * sg));
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = sum_rows32(sum_rows16(acc[i] * sg));
+  if (grp == 0) {
+    unsigned w[DPL / 2];
+#pragma unroll
+    for (int i = 0; i < DPL / 2; ++i)
+      w[i] = pack2(f32_to_16<BF>(acc[2 * i] * inv), f32_to_16<BF>(acc[2 * i + 1] * inv));
+    if constexpr (DPL == 8)
+      *(u32x4*)orow = u32x4{w[0], w[1], w[2], w[3]};
+    else
+      *(u32x2*)orow = u32x2{w[0], w[1]};
+  }
 }
 
 // ------------------------------------------------------------------ KV write scatter

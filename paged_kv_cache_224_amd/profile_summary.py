@@ -1,0 +1,114 @@
+"""Turn rocprofv3 output of the benchmark into the short summaries kept under profiles/.
+
+Usage (from the repository root, after the commands that ``commands()`` lists have written
+their CSV files under OUT on an MI355X):
+
+    python -m paged_kv_cache_224_amd.profile_summary OUT WORKLOAD [SCHEDULE]
+
+writes profiles/pa_decode_<WORKLOAD>.md (kernel statistics, HBM counters scaled by a plain
+device copy of known size, the benchmark line) and profiles/pa_decode_<WORKLOAD>_traffic.json
+(measured HBM bytes per decode launch, keyed by the kernel source hash; bench.py reports it as
+``roofline.traffic`` while the source is unchanged).  Reads CSV and JSON text only.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "paged_kv_cache_224_amd", "csrc", "pagedkv.hip")
+COPY_MIB = 1024
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+
+
+def commands(workload: str, schedule: str, out: str = "OUT") -> list:
+    """The profiling commands whose output summarize() reads (run from the repository root)."""
+    b = f"python -u bench.py --workload {workload} --schedule {schedule} --no-cpu-baseline"
+    return [
+        f"python -u bench.py --workload {workload} --schedule {schedule} --no-cpu-baseline > {out}/bench.json",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/kt -o run -- {b}",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/fetch -o run -- {b} --steps 10 --warmup 3",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- {b} --steps 10 --warmup 3",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/copyf -o run -- python -u bench.py "
+        f"--copy-reference {COPY_MIB}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/copyw -o run -- python -u bench.py "
+        f"--copy-reference {COPY_MIB}",
+    ]
+
+
+def _counter(path: str, name: str) -> dict:
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == name:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize(out: str, workload: str, schedule: str = "balanced") -> str:
+    ks = list(csv.DictReader(open(os.path.join(out, "kt", "run_kernel_stats.csv"))))
+    fetch = _counter(os.path.join(out, "fetch", "run_counter_collection.csv"), "FETCH_SIZE")
+    write = _counter(os.path.join(out, "write", "run_counter_collection.csv"), "WRITE_SIZE")
+    cf = _counter(os.path.join(out, "copyf", "run_counter_collection.csv"), "FETCH_SIZE")
+    cw = _counter(os.path.join(out, "copyw", "run_counter_collection.csv"), "WRITE_SIZE")
+    copy_name = [k for k in cf if "copyBuffer" in k][0]
+    true_kib = COPY_MIB * 1024
+    ff, wf = true_kib / cf[copy_name], true_kib / cw[copy_name]
+    bench = json.loads(open(os.path.join(out, "bench.json")).read().strip().splitlines()[-1])
+    h = source_hash()
+
+    lines = [f"# {workload}: rocprofv3 summary of the benchmark step ({schedule} schedule)", "",
+             f"Kernel source sha256[:16] = `{h}` (paged_kv_cache_224_amd/csrc/pagedkv.hip)", "",
+             "## Commands (run from the repository root on one MI355X; OUT is any scratch folder)", "",
+             "```"] + commands(workload, schedule) + [
+             f"python -m paged_kv_cache_224_amd.profile_summary OUT {workload} {schedule}", "```", "",
+             "## Kernel statistics (--kernel-trace --stats)", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in ks:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} |")
+    lines += ["", "## HBM counters (KiB per dispatch, mean over dispatches)", "",
+              f"Calibration: a {COPY_MIB} MiB device copy reads {cf[copy_name]:.0f} KiB by FETCH_SIZE and writes "
+              f"{cw[copy_name]:.0f} KiB by WRITE_SIZE, so FETCH_SIZE is scaled by {ff:.3f} and WRITE_SIZE by "
+              f"{wf:.3f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | written bytes (scaled) |",
+              "|---|---|---|---|---|"]
+    scaled = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "copyBuffer" in k or "elementwise" in k or "fill" in k:
+            continue
+        f, w = fetch.get(k, 0.0), write.get(k, 0.0)
+        rb, wb = f * ff * 1024, w * wf * 1024
+        scaled[k] = (rb, wb)
+        lines.append(f"| {k[:90]} | {f:.1f} | {w:.1f} | {rb / 1e6:.2f} MB | {wb / 1e6:.2f} MB |")
+    dk = [k for k in scaled if "decode" in k][0]
+    rb, wb = scaled[dk]
+    alg = bench["roofline"]["bytes_per_launch"]
+    trace_avg = [float(r["AverageNs"]) for r in ks if "decode" in r["Name"]][0]
+    lines += ["", f"Decode kernel: HBM traffic {(rb + wb) / 1e6:.2f} MB per launch (read {rb / 1e6:.2f} + "
+                  f"written {wb / 1e6:.2f}) against {alg / 1e6:.2f} MB algorithmic bytes "
+                  f"({(rb + wb) / alg:.3f}x).  Kernel-trace average {trace_avg / 1e3:.1f} us = "
+                  f"{alg / trace_avg:.0f} GB/s algorithmic; the benchmark's HIP events give "
+                  f"{bench['decode_kernel_ms_mean'] * 1e3:.1f} us.", "",
+              "## Benchmark line of the same build", "", "```json", json.dumps(bench), "```", ""]
+    text = "\n".join(lines)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"pa_decode_{workload}.md"), "w") as fh:
+        fh.write(text)
+    with open(os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.json"), "w") as fh:
+        json.dump({"kernel_source_sha256_16": h, "workload": workload, "schedule": schedule,
+                   "decode_traffic_bytes": rb + wb, "decode_read_bytes": rb, "decode_write_bytes": wb,
+                   "fetch_scale": ff, "write_scale": wf, "trace_average_ns": trace_avg}, fh, indent=1)
+    return text
+
+
+if __name__ == "__main__":
+    if len(sys.argv) < 3:
+        sys.exit(__doc__)
+    print(summarize(sys.argv[1], sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "balanced"))
