@@ -229,7 +229,12 @@ struct Tile {
   static constexpr int VLD = ROWB / 64;                     // 16-byte V loads per lane
   static constexpr int TPI = 64 / CPRS;                     // tokens covered by one V load
   static constexpr int CPR = D / 8;                         // 16-byte chunks per LDS row (16-bit)
-  static constexpr int LDS_BYTES = 16 * D * 2;
+  static constexpr int VLDS = 16 * D * 2;                   // the V tile
+  static constexpr int QLDS = NS * 64 * 16;                 // one segment's q operand
+  static constexpr int LDS_BYTES = VLDS + QLDS;             // per wave
+  // Tiles in flight per wave.  An fp8 tile is half the bytes of a 16-bit one, so it keeps
+  // two in flight to hold the same bytes per wave against the load latency.
+  static constexpr int PF = (KV == KFP8) ? 2 : 1;
 };
 
 // LDS slot (16-byte unit) of chunk c of token row t; XOR swizzle spreads the transposed
@@ -361,6 +366,7 @@ void pa_decode_kernel(DecodeParams a) {
   const int g = blockIdx.y * kMaxWaves + wl;               // KV head of this wave
   if (g >= a.Hkv) return;
   char* vtile = smem + wl * TL::LDS_BYTES;
+  char* qstage = vtile + TL::VLDS;                          // next segment's q, lane-major
   const int cap = a.cap;
 
   // ---- the workgroup's segments
@@ -615,9 +621,16 @@ void pa_decode_kernel(DecodeParams a) {
     return;
   }
 
-  // ---- prologue: q of the first segment, the first tile's block id and the first tile
-  u32x4 qc[TL::NS];
+  // ---- prologue: q of the first segment, the first tile's block id and the first tiles.
+  // The next segment's q goes through LDS: loaded into qn at a segment switch, written to the
+  // wave's LDS stage one tile later (when the load has landed, so the write does not drain
+  // the tiles in flight), and read back into qc at the next switch.  Registers loaded from
+  // memory are never copied, which would force a wait right after the load.
+  Seg nxt = src.next(cur, lane);
+  u32x4 qc[TL::NS], qn[TL::NS];
   load_q(cur.b, qc);
+  bool qpend = nxt.valid;
+  if (qpend) load_q(nxt.b, qn);
 
   // Issue iterator: (iseg, itile) is the next tile to load; its block id sits in `nid`,
   // loaded one tile ahead of the tile's own loads, so reading it never waits for loads that
@@ -647,29 +660,46 @@ void pa_decode_kernel(DecodeParams a) {
     nid = load_id(iseg.b, itile);
   };
 
-  u32x4 kr[TL::KLD], vr[TL::VLD];
-  issue(kr, vr);
+  // PF register sets of K/V rows rotate through the loop: set r is computed, then refilled
+  // with the tile PF positions ahead, so PF tiles stay in flight per wave.
+  u32x4 kr[TL::PF][TL::KLD], vr[TL::PF][TL::VLD];
+#pragma unroll
+  for (int r = 0; r < TL::PF; ++r) issue(kr[r], vr[r]);
 
   int tile = cur.tlo;
-  for (;;) {
-    const f32x4 sc = part1(kr, vr, qc);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(kr, vr);                                      // the tile registers are free again
-    __builtin_amdgcn_sched_barrier(0);
-    part2(tile, cur.n, sc);
-    if (tile + 1 < cur.thi) {
-      ++tile;
-      continue;
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int r = 0; r < TL::PF; ++r) {
+      const f32x4 sc = part1(kr[r], vr[r], qc);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kr[r], vr[r]);                              // set r is free again
+      __builtin_amdgcn_sched_barrier(0);
+      part2(tile, cur.n, sc);
+      if (qpend) {
+#pragma unroll
+        for (int s = 0; s < TL::NS; ++s) *(u32x4*)(qstage + (s * 64 + lane) * 16) = qn[s];
+        qpend = false;
+      }
+      if (tile + 1 < cur.thi) {
+        ++tile;
+        continue;
+      }
+      finalize(cur);
+      if (!nxt.valid) {
+        done = true;
+        break;
+      }
+      // next segment: its q is in the LDS stage; the q of the one after it is loaded now
+      reset();
+      cur = nxt;
+#pragma unroll
+      for (int s = 0; s < TL::NS; ++s) qc[s] = *(const u32x4*)(qstage + (s * 64 + lane) * 16);
+      nxt = src.next(cur, lane);
+      qpend = nxt.valid;
+      if (qpend) load_q(nxt.b, qn);
+      tile = cur.tlo;
     }
-    finalize(cur);
-    const Seg nx = src.next(cur, lane);
-    if (!nx.valid) break;
-    // next segment: its q is loaded now and first used after the next tile's loads, which
-    // were issued before it, have landed
-    reset();
-    cur = nx;
-    load_q(cur.b, qc);
-    tile = cur.tlo;
   }
 }
 
