@@ -57,7 +57,11 @@ typedef enum {
   PKV_ERR_ALIGN = -4,      /* a pointer is not aligned as required */
   PKV_ERR_WORKSPACE = -5,  /* split-K buffers missing */
   PKV_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch */
-  PKV_ERR_CHECK = -7       /* PKV_CHECK=1 found an invalid device-resident value */
+  PKV_ERR_CHECK = -7,      /* PKV_CHECK=1 found an invalid device-resident value */
+  PKV_ERR_STATE = -8,      /* block manager: sequence id in use, or sequence in the wrong state */
+  PKV_ERR_NOT_FOUND = -9,  /* block manager: unknown sequence id */
+  PKV_ERR_NO_SPACE = -10,  /* block manager: not enough free blocks */
+  PKV_ERR_HOST = -11       /* a host buffer is not pinned, device-mapped memory of the needed size */
 } pkv_status;
 
 /*
@@ -153,6 +157,94 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                       int max_context_len, int partition_size, int out_dtype, void* stream);
+
+/*
+ * paged_kv_copy_blocks -- copy whole blocks inside the K and V pools (the data side of
+ * copy-on-write: "vllm-project-vllm -- L2", section 9 "Memory Management", COW sharing and
+ * the COW fork for parallel sampling; the block manager below reports which copies a step
+ * needs).
+ *
+ * For i < num_pairs: K[dst_blocks[i]] = K[src_blocks[i]] and V[dst_blocks[i]] =
+ * V[src_blocks[i]], each block being block_size * num_kv_heads * head_dim elements of
+ * cache_dtype (copied as bytes).  Every copy reads the pools as they were before the call:
+ * destinations must be distinct and must not appear among the sources (otherwise the result
+ * is unspecified).  A pair with an id outside [0, num_blocks) is skipped.
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim], device
+ *   src_blocks, dst_blocks  [num_pairs] int32, device
+ * block_size * num_kv_heads * head_dim * element bytes must be a multiple of 16.  PKV_CHECK=1
+ * validates ranges and distinctness on the host (PKV_ERR_CHECK).
+ */
+int paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int num_pairs, int num_blocks, int block_size,
+                         int num_kv_heads, int head_dim, int cache_dtype, void* stream);
+
+/*
+ * paged_kv_swap_blocks -- move whole blocks between the device pools and pinned host pools
+ * (swapping a preempted sequence's blocks to CPU memory and back: "vllm-project-vllm -- L2",
+ * section 9 "Memory Management", preemptive scheduling and KV offload).
+ *
+ * to_host = 1: HK[host_blocks[i]] = K[dev_blocks[i]] (and V likewise); to_host = 0: the
+ * reverse.  Targets must be distinct.  A pair with an id outside its pool is skipped.
+ *   host_key, host_value  [num_host_blocks, block_size, num_kv_heads, head_dim] in pinned
+ *                         host memory (hipHostMalloc, or a pinned torch tensor); the library
+ *                         reads/writes it through its device mapping, so the transfer crosses
+ *                         the host link.  PKV_ERR_HOST if the memory is not pinned and mapped
+ *                         or the allocation is smaller than the pool.
+ *   dev_blocks, host_blocks  [num_pairs] int32, device
+ * Ordering: asynchronous on `stream` like every call; the host pool is complete after the
+ * stream is synchronised.
+ */
+int paged_kv_swap_blocks(void* key_cache, void* value_cache, void* host_key, void* host_value,
+                         const int32_t* dev_blocks, const int32_t* host_blocks, int num_pairs,
+                         int num_blocks, int num_host_blocks, int block_size, int num_kv_heads,
+                         int head_dim, int cache_dtype, int to_host, void* stream);
+
+/*
+ * Block manager -- host-side bookkeeping of the pool ("vllm-project-vllm -- L2", section 9
+ * "Memory Management"; section 8 on the block-table invariant; section 11 steps 2 and 5).
+ *
+ * A sequence owns ceil(num_tokens / block_size) blocks, so at most block_size - 1 of its
+ * slots are unused; appending a token allocates a block only when the last one is full.
+ * A fork shares the parent's blocks (reference counts, no data copied); appending into a
+ * shared last block first moves the appender to a fresh copy (copy-on-write), reported as a
+ * (src, dst) pair for paged_kv_copy_blocks.  Invariant, checked by pkv_bm_check: every
+ * device block is free (count 0, in the free set) or referenced exactly count times by
+ * sequence tables.  Swap-out moves every block of a sequence to the host pool (shared blocks
+ * are copied, the device copies stay with their other owners); swap-in brings them back into
+ * fresh device blocks.
+ * Policy (not fixed by the pages): the lowest-numbered free block is always taken first.
+ * The handle is not thread-safe; every call is host-only and synchronous.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* num_blocks device blocks and num_host_blocks host blocks of block_size tokens; NULL on
+   a bad size or out of memory. */
+pkv_block_manager* pkv_bm_create(int num_blocks, int block_size, int num_host_blocks);
+void pkv_bm_destroy(pkv_block_manager* bm);
+int pkv_bm_num_free(const pkv_block_manager* bm);
+int pkv_bm_num_free_host(const pkv_block_manager* bm);
+/* New sequence holding num_tokens tokens (a prompt): ceil(num_tokens / block_size) blocks. */
+int pkv_bm_add(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens);
+/* Append one token: *slot = block * block_size + offset of its cache row.  If the last block
+   was shared, *copy_src / *copy_dst name the copy to make before writing (else both -1). */
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, int64_t* slot, int32_t* copy_src,
+                  int32_t* copy_dst);
+/* child shares the parent's first num_tokens tokens (num_tokens < 0: all of them). */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child, int64_t num_tokens);
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
+/* Move a sequence's blocks out to / back from the host pool.  Fills (dev_blocks[i],
+   host_blocks[i]) pairs for paged_kv_swap_blocks and returns their number (or an error). */
+int pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* dev_blocks, int32_t* host_blocks,
+                    int capacity);
+int pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* host_blocks, int32_t* dev_blocks,
+                   int capacity);
+int pkv_bm_num_tokens(const pkv_block_manager* bm, int64_t seq_id, int64_t* num_tokens);
+/* Host arrays: block_tables [num_seqs, max_blocks] (entries past a sequence's blocks are 0)
+   and context_lens [num_seqs] of the listed (resident) sequences. */
+int pkv_bm_table(const pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                 int32_t* block_tables, int max_blocks, int32_t* context_lens);
+/* PKV_OK if the invariant above and the block-count bound hold, else PKV_ERR_CHECK. */
+int pkv_bm_check(const pkv_block_manager* bm);
 
 /* Partial slots per (sequence, head) a split-K schedule needs (0 for partition_size == 0). */
 int paged_attn_partial_slots(int max_context_len, int partition_size);

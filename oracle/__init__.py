@@ -186,3 +186,27 @@ def fp8_decode(codes) -> np.ndarray:
 def quantize_pool(pool: torch.Tensor, scale: float) -> torch.Tensor:
     """Whole-pool fp8 quantisation, element by element through fp8_encode."""
     return fp8_encode(pool, scale).view(pool.shape)
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src, dst) -> None:
+    """Copy-on-write data copies ("vllm-project-vllm -- L2", section 9, COW sharing): block
+    dst[i] of each pool becomes block src[i] as the pools were before the call.  In place on
+    CPU pools [num_blocks, block_size, Hkv, D] of any dtype (bytes are moved unchanged)."""
+    k0, v0 = k_cache.clone(), v_cache.clone()
+    for s, d in zip(np.asarray(src).tolist(), np.asarray(dst).tolist()):
+        k_cache[d] = k0[s]
+        v_cache[d] = v0[s]
+
+
+def swap_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, host_k: torch.Tensor, host_v: torch.Tensor,
+                dev_blocks, host_blocks, to_host: bool) -> None:
+    """Swapping blocks to host memory and back ("vllm-project-vllm -- L2", section 9):
+    to_host copies device block dev_blocks[i] into host block host_blocks[i], else the reverse.
+    In place on CPU tensors of the same block shape."""
+    for d, h in zip(np.asarray(dev_blocks).tolist(), np.asarray(host_blocks).tolist()):
+        if to_host:
+            host_k[h] = k_cache[d]
+            host_v[h] = v_cache[d]
+        else:
+            k_cache[d] = host_k[h]
+            v_cache[d] = host_v[h]

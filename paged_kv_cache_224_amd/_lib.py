@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_ERR_SHAPE = -2
 _DT = {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3,
        torch.float8_e4m3fn: PKV_FP8_E4M3}
 
@@ -52,6 +53,29 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_balanced_split.restype = I
         L.pkv_status_string.argtypes = [I]
         L.pkv_status_string.restype = ctypes.c_char_p
+        L.paged_kv_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+        L.paged_kv_copy_blocks.restype = I
+        L.paged_kv_swap_blocks.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+        L.paged_kv_swap_blocks.restype = I
+        I64, PI64, PI32 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+        L.pkv_bm_create.argtypes = [I, I, I]
+        L.pkv_bm_create.restype = P
+        L.pkv_bm_destroy.argtypes = [P]
+        L.pkv_bm_destroy.restype = None
+        for fn in ("pkv_bm_num_free", "pkv_bm_num_free_host", "pkv_bm_check"):
+            getattr(L, fn).argtypes = [P]
+            getattr(L, fn).restype = I
+        L.pkv_bm_add.argtypes = [P, I64, I64]
+        L.pkv_bm_append.argtypes = [P, I64, PI64, PI32, PI32]
+        L.pkv_bm_fork.argtypes = [P, I64, I64, I64]
+        L.pkv_bm_free.argtypes = [P, I64]
+        L.pkv_bm_swap_out.argtypes = [P, I64, PI32, PI32, I]
+        L.pkv_bm_swap_in.argtypes = [P, I64, PI32, PI32, I]
+        L.pkv_bm_num_tokens.argtypes = [P, I64, PI64]
+        L.pkv_bm_table.argtypes = [P, PI64, I, PI32, I, PI32]
+        for fn in ("pkv_bm_add", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out",
+                   "pkv_bm_swap_in", "pkv_bm_num_tokens", "pkv_bm_table"):
+            getattr(L, fn).restype = I
         _lib = L
     return _lib
 
@@ -177,3 +201,114 @@ def decode(out: torch.Tensor, query, key_cache, value_cache, block_tables, conte
     if PS != 0:
         paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens, ws.max_context_len, PS,
                           stream)
+
+
+def paged_kv_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, src_blocks: torch.Tensor,
+                         dst_blocks: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks inside both pools (copy-on-write); src/dst are int32 device tensors."""
+    NB, BS, Hkv, D = key_cache.shape
+    if value_cache.shape != key_cache.shape or src_blocks.shape != dst_blocks.shape:
+        raise ValueError("shape mismatch")
+    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32:
+        raise ValueError("block ids must be int32")
+    rc = lib().paged_kv_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(src_blocks), _ptr(dst_blocks),
+                                    src_blocks.numel(), NB, BS, Hkv, D, _DT[key_cache.dtype], _stream(stream))
+    _check("paged_kv_copy_blocks", rc)
+
+
+def paged_kv_swap_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, host_key: torch.Tensor,
+                         host_value: torch.Tensor, dev_blocks: torch.Tensor, host_blocks: torch.Tensor,
+                         to_host: bool, stream=None) -> None:
+    """Move whole blocks between the device pools and pinned host pools (same block shape).
+
+    host_key / host_value must be pinned CPU tensors (pin_memory=True); ids are int32 device
+    tensors."""
+    NB, BS, Hkv, D = key_cache.shape
+    NH = host_key.shape[0]
+    if host_key.shape[1:] != key_cache.shape[1:] or host_value.shape != host_key.shape:
+        raise ValueError("host pools must have the device pools' block shape")
+    if host_key.dtype != key_cache.dtype or not (host_key.is_pinned() and host_value.is_pinned()):
+        raise ValueError("host pools must be pinned and of the cache dtype")
+    rc = lib().paged_kv_swap_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(host_key), _ptr(host_value),
+                                    _ptr(dev_blocks), _ptr(host_blocks), dev_blocks.numel(), NB, NH, BS, Hkv, D,
+                                    _DT[key_cache.dtype], 1 if to_host else 0, _stream(stream))
+    _check("paged_kv_swap_blocks", rc)
+
+
+class BlockManager:
+    """Host block manager of the native library (see include/pagedkv.h: refcounted blocks,
+    copy-on-write forks, swap bookkeeping, lowest-free-block-first allocation)."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
+        self._h = lib().pkv_bm_create(num_blocks, block_size, num_host_blocks)
+        if not self._h:
+            raise PagedKVError("pkv_bm_create", PKV_ERR_SHAPE, "bad sizes or out of memory")
+        self.num_blocks, self.block_size, self.num_host_blocks = num_blocks, block_size, num_host_blocks
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pkv_bm_destroy(h)
+            self._h = None
+
+    def _call(self, fn, *args):
+        rc = getattr(lib(), fn)(self._h, *args)
+        if rc < 0:
+            raise PagedKVError(fn, rc, status_string(rc))
+        return rc
+
+    def num_free(self) -> int:
+        return self._call("pkv_bm_num_free")
+
+    def num_free_host(self) -> int:
+        return self._call("pkv_bm_num_free_host")
+
+    def add(self, seq_id: int, num_tokens: int) -> None:
+        self._call("pkv_bm_add", seq_id, num_tokens)
+
+    def append(self, seq_id: int):
+        """-> (slot, copy_src, copy_dst); copy ids are -1 when no copy-on-write was needed."""
+        slot, cs, cd = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        self._call("pkv_bm_append", seq_id, ctypes.byref(slot), ctypes.byref(cs), ctypes.byref(cd))
+        return slot.value, cs.value, cd.value
+
+    def fork(self, parent: int, child: int, num_tokens: int = -1) -> None:
+        self._call("pkv_bm_fork", parent, child, num_tokens)
+
+    def free(self, seq_id: int) -> None:
+        self._call("pkv_bm_free", seq_id)
+
+    def num_tokens(self, seq_id: int) -> int:
+        n = ctypes.c_int64()
+        self._call("pkv_bm_num_tokens", seq_id, ctypes.byref(n))
+        return n.value
+
+    def _swap(self, fn, seq_id, capacity):
+        a = (ctypes.c_int32 * max(1, capacity))()
+        b = (ctypes.c_int32 * max(1, capacity))()
+        n = self._call(fn, seq_id, a, b, capacity)
+        return list(a[:n]), list(b[:n])
+
+    def swap_out(self, seq_id: int, capacity: int = 1 << 16):
+        """-> (device blocks, host blocks) to copy device -> host."""
+        return self._swap("pkv_bm_swap_out", seq_id, capacity)
+
+    def swap_in(self, seq_id: int, capacity: int = 1 << 16):
+        """-> (host blocks, device blocks) to copy host -> device."""
+        return self._swap("pkv_bm_swap_in", seq_id, capacity)
+
+    def table(self, seq_ids, max_blocks: int):
+        """-> (block_tables int32 [n, max_blocks], context_lens int32 [n]) as numpy arrays."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        bt = np.zeros((len(ids), max_blocks), dtype=np.int32)
+        lens = np.zeros(len(ids), dtype=np.int32)
+        self._call("pkv_bm_table", ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(ids),
+                   bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), max_blocks,
+                   lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        return bt, lens
+
+    def check(self) -> bool:
+        """True if the reference-count invariant and the per-sequence block bound hold."""
+        rc = lib().pkv_bm_check(self._h)
+        return rc == 0

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce",
+    assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce", "paged_kv_copy_blocks",
+                          "paged_kv_swap_blocks", "pkv_bm_create", "pkv_bm_append", "pkv_bm_check",
                           "paged_attn_workspace_bytes", "paged_attn_partial_slots",
                           "paged_attn_balanced_split", "pkv_status_string"}
     L = ctypes.CDLL(_lib.LIB_PATH)
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert pk.status_string(0) == "ok"
-    for s in range(-7, 0):
+    for s in range(-11, 0):
         assert pk.status_string(s) not in ("ok", "unknown status")
     assert pk.status_string(-99) == "unknown status"
 
@@ -134,6 +135,46 @@ def test_reduce_rejects(kw, want):
     args = dict(out=A, tmp=A, ml=A, es=A, lens=A, B=4, Hq=8, D=64, maxlen=256, PS=64, odt=0, stream=None)
     args.update(kw)
     assert pk.lib().paged_attn_reduce(*args.values()) == want
+
+
+def _copy(**kw):
+    args = dict(kc=A, vc=A, src=A, dst=A, n=4, NB=80, BS=16, Hkv=2, D=64, dt=1, stream=None)
+    args.update(kw)
+    return pk.lib().paged_kv_copy_blocks(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=5), E_DTYPE),
+    (dict(BS=1, Hkv=1, D=4), E_SHAPE),         # 8-byte blocks: not a multiple of 16
+    (dict(n=-1), E_SHAPE),
+    (dict(src=None), E_NULL),
+    (dict(kc=MIS), E_ALIGN),
+    (dict(dst=A + 2), E_ALIGN),
+])
+def test_copy_blocks_rejects(kw, want):
+    assert _copy(**kw) == want
+
+
+def test_copy_blocks_zero_pairs_is_a_noop():
+    assert _copy(n=0, src=None, dst=None) == OK
+
+
+def _swap(**kw):
+    args = dict(kc=A, vc=A, hk=A, hv=A, dev=A, host=A, n=4, NB=80, NH=40, BS=16, Hkv=2, D=64, dt=1,
+                to_host=1, stream=None)
+    args.update(kw)
+    return pk.lib().paged_kv_swap_blocks(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(to_host=2), E_SHAPE),
+    (dict(NH=-1), E_SHAPE),
+    (dict(dt=9), E_DTYPE),
+    (dict(hk=None), E_NULL),
+    (dict(hv=MIS), E_ALIGN),
+])
+def test_swap_blocks_rejects(kw, want):
+    assert _swap(**kw) == want
 
 
 def test_binding_raises_on_error_status():
