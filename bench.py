@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per pool copy)")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "swap"],
+                    help="decode: the decode step (default); copy_blocks / swap: the whole-block operations "
+                         "on a pool of the workload's block shape")
+    ap.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks / swap call")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only copy a buffer of this size 5 times (reference for HBM traffic counters)")
     return ap.parse_args()
@@ -114,6 +118,94 @@ def cpu_baseline(w, min_seconds):
     return t, threads, reps
 
 
+def block_ops(args):
+    """Whole-block operations on pools of the workload's block shape: copy-on-write copies
+    (HBM, read + write) or swap out to / in from pinned host memory (host link)."""
+    cfg = I.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    fp8 = cfg.kv_dtype == "fp8"
+    dt = torch.uint8 if fp8 else I.DTYPES[cfg.kv_dtype]
+    n = args.pairs
+    NB = 2 * n + 16
+    shape = (NB, cfg.block_size, cfg.Hkv, cfg.D)
+    kc = torch.zeros(shape, dtype=dt, device=dev)
+    vc = torch.zeros_like(kc)
+    block_bytes = cfg.block_size * cfg.Hkv * cfg.D * (1 if fp8 else 2)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(NB).astype(np.int32)
+    a = torch.from_numpy(perm[:n].copy()).to(dev)
+    b = torch.from_numpy(perm[n:2 * n].copy()).to(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    res = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8" if fp8 else cfg.kv_dtype, "data": "synthetic",
+           "config": {"workload": f"{cfg.name} block shape", "op": args.op, "pairs": n, "block_bytes": block_bytes,
+                      "pools": 2}}
+    if args.op == "copy_blocks":
+        def run():
+            pk.paged_kv_copy_blocks(kc, vc, a, b)
+        moved = 2 * 2 * n * block_bytes                 # read + write, K and V
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            run()
+            e[1].record()
+        torch.cuda.synchronize()
+        t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+        gbps = moved / t / 1e9
+        res.update({"metric": "copy_blocks HBM GB/s (read + write)", "value": round(gbps, 1), "unit": "GB/s",
+                    "ms_per_step": round(t * 1e3, 4),
+                    "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                                 "kernel": "copy_blocks_kernel", "bytes_per_launch": moved}})
+    else:
+        NH = n + 16
+        hk = torch.zeros((NH,) + shape[1:], dtype=dt, pin_memory=True)
+        hv = torch.zeros((NH,) + shape[1:], dtype=dt, pin_memory=True)
+        hid = torch.from_numpy(rng.permutation(NH)[:n].astype(np.int32)).to(dev)
+        moved = 2 * n * block_bytes                     # K and V blocks across the link, one way
+        out = {}
+        for direction in ("out", "in"):
+            def run():
+                pk.paged_kv_swap_blocks(kc, vc, hk, hv, a, hid, to_host=direction == "out")
+            for _ in range(args.warmup):
+                run()
+            torch.cuda.synchronize()
+            for e in ev:
+                e[0].record()
+                run()
+                e[1].record()
+            torch.cuda.synchronize()
+            out[direction] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+        # reference: one contiguous pinned <-> device copy of the same bytes (DMA engines)
+        flat_d = torch.empty(moved, dtype=torch.uint8, device=dev)
+        flat_h = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+        ref = {}
+        for direction in ("out", "in"):
+            for _ in range(2):
+                (flat_h.copy_(flat_d, non_blocking=True) if direction == "out" else flat_d.copy_(flat_h, non_blocking=True))
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(5):
+                (flat_h.copy_(flat_d, non_blocking=True) if direction == "out" else flat_d.copy_(flat_h, non_blocking=True))
+            torch.cuda.synchronize()
+            ref[direction] = (time.perf_counter() - t0) / 5
+        g_out, g_in = moved / out["out"] / 1e9, moved / out["in"] / 1e9
+        r_out, r_in = moved / ref["out"] / 1e9, moved / ref["in"] / 1e9
+        res.update({"metric": "block swap GB/s over the host link (out = device to host)",
+                    "value": round(min(g_out, g_in), 2), "unit": "GB/s",
+                    "ms_per_step": round((out["out"] + out["in"]) * 1e3, 4),
+                    "swap_out_gbps": round(g_out, 2), "swap_in_gbps": round(g_in, 2),
+                    "contiguous_dma_copy_gbps": {"out": round(r_out, 2), "in": round(r_in, 2)},
+                    "roofline": {"bound": "host link", "achieved": round(min(g_out, g_in), 2),
+                                 "peak": round(min(r_out, r_in), 2), "unit": "GB/s",
+                                 "frac": round(min(g_out / r_out, g_in / r_in), 4), "traffic": None,
+                                 "kernel": "swap_blocks_kernel", "bytes_per_launch": moved,
+                                 "peak_is": "contiguous pinned<->device copy of the same bytes, measured"}})
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -124,6 +216,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_reference:
         copy_reference(args.copy_reference)
+        return
+    if args.op != "decode":
+        block_ops(args)
         return
     dev = torch.device("cuda:0")
     cfg = I.CONFIGS[args.workload]

@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = [os.path.join(HERE, "csrc", "pagedkv.hip"), os.path.join(HERE, "csrc", "block_manager.cpp")]
+SRC = [os.path.join(HERE, "csrc", n) for n in ("pagedkv.hip", "block_ops.hip", "block_manager.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpagedkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
