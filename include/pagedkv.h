@@ -145,14 +145,42 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
                       float* max_logits, float* exp_sums, void* stream);
 
 /*
+ * paged_attn_multi_query -- q_len new query tokens per sequence against its paged KV cache,
+ * causal among themselves (scoring k speculative draft tokens in one pass: "vLLM vs vllm",
+ * speculative decoding; several new tokens of a sequence at once: "vllm-project-vllm -- L2",
+ * chunked prefill in the mechanisms table).
+ *
+ * The L = q_len new tokens are the last L of the n = context_lens[b] cached tokens (their K/V
+ * rows are already in the pools).  New token i < L sits at position n - L + i and attends to
+ * the tokens t < n - L + 1 + i, i.e. to itself and everything before it; with no visible
+ * token the row is 0.  With L = 1 this is paged_attn_decode.
+ *   query  [num_seqs, q_len, num_heads, head_dim]
+ *   out    [num_seqs, q_len, num_heads, head_dim] (written when partition_size == 0)
+ *   split-K partials as for paged_attn_decode with num_heads' = q_len * num_heads rows per
+ *   sequence ([num_seqs, q_len, num_heads, Pslots, ...]); paged_attn_reduce called with
+ *   num_heads = q_len * num_heads forms `out`.
+ * Every other argument, the supported set and the error behaviour are those of
+ * paged_attn_decode, plus: 1 <= q_len and (num_heads / num_kv_heads) * q_len <= 16 (the query
+ * heads of one KV group times the new tokens fill at most the 16 columns of one MFMA tile).
+ */
+int paged_attn_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                           int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
+                           float k_scale, float v_scale, int max_context_len, int partition_size,
+                           float* tmp_out, float* max_logits, float* exp_sums, void* stream);
+
+/*
  * paged_attn_reduce -- merge split-K partials by log-sum-exp weighting.
  *
  * For every (b, h), with P the number of partials paged_attn_decode wrote for sequence b
  * under the same partition_size (ceil(n / partition_size) for fixed partitions; the number of
  * ranges the sequence's tiles fall in for a balanced split, recomputed from context_lens):
  *   M = max_{p<P} m_p,  w_p = l_p * exp(m_p - M),  out[b][h] = sum_p w_p o_p / sum_p w_p
- * rounded to out_dtype (nearest even).  P = 0 gives a zero row.  Partials with p >= P are
- * never read.  Buffers and Pslots as in paged_attn_decode.
+ * rounded to out_dtype (nearest even).  P = 0, or partials that all saw no token (m = -inf,
+ * l = 0, from the causal rows of paged_attn_multi_query), give a zero row.  Partials with
+ * p >= P are never read.  Buffers and Pslots as in paged_attn_decode; num_heads counts the
+ * output rows per sequence (q_len * heads after paged_attn_multi_query).
  */
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,

@@ -210,3 +210,23 @@ def swap_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, host_k: torch.Tens
         else:
             k_cache[d] = host_k[h]
             v_cache[d] = host_v[h]
+
+
+def attn_multi_query(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: np.ndarray,
+                     context_lens: np.ndarray, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                     kv_dtype: Optional[str] = None, nthreads: Optional[int] = None) -> np.ndarray:
+    """fp64 [B, L, Hq, D] for L new query tokens per sequence, causal among themselves.
+
+    Speculative verification scores k draft tokens in one pass ("vLLM vs vllm", speculative
+    decoding) and chunked prefill feeds several new tokens of a sequence at once ("L2", the
+    mechanisms table): the L new tokens are the last L of the sequence's n cached tokens, and
+    new token i (position n - L + i) sees exactly the tokens up to and including itself.  So
+    query i is a one-token decode over the first clip(n - L + 1 + i, 0, n) tokens."""
+    B, L, Hq, D = q.shape
+    lens = np.asarray(context_lens, dtype=np.int64)
+    out = np.zeros((B, L, Hq, D), dtype=np.float64)
+    for i in range(L):
+        vis = np.clip(lens - L + 1 + i, 0, lens).astype(np.int32)
+        out[:, i] = attn(q[:, i].contiguous(), k_cache, v_cache, block_tables, vis, scale, k_scale, v_scale,
+                         kv_dtype, nthreads)
+    return out

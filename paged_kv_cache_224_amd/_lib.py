@@ -43,6 +43,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, F, F, I, I, P, P,
                                         P, P]
         L.paged_attn_decode.restype = I
+        L.paged_attn_multi_query.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, I, F, F, I, I, P, P,
+                                             P, P]
+        L.paged_attn_multi_query.restype = I
         L.paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         L.paged_attn_reduce.restype = I
         L.paged_attn_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -157,6 +160,42 @@ def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cach
                                  float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
                                  _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _stream(stream))
     _check("paged_attn_decode", rc)
+
+
+def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key_cache: torch.Tensor,
+                           value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: float, max_context_len: int, partition_size: int = 0,
+                           tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
+                           exp_sums: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                           stream=None) -> None:
+    """query [B, L, Hq, D]: L new tokens per sequence, causal among themselves (include/pagedkv.h)."""
+    B, Lq, Hq, D = query.shape
+    NB, BS, Hkv, D2 = key_cache.shape
+    if D2 != D or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    rc = lib().paged_attn_multi_query(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                      _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Lq, Hq,
+                                      Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
+                                      float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
+                                      _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _stream(stream))
+    _check("paged_attn_multi_query", rc)
+
+
+def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, context_lens, scale,
+                ws: "DecodeWorkspace", k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """paged_attn_multi_query, then paged_attn_reduce over q_len * Hq rows when split-K.
+
+    ws must be a DecodeWorkspace for (num_seqs, q_len * num_heads, ...)."""
+    PS = ws.partition_size
+    B, Lq, Hq, D = query.shape
+    paged_attn_multi_query(out if PS == 0 else None, query, key_cache, value_cache, block_tables, context_lens,
+                           scale, ws.max_context_len, PS, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale, v_scale,
+                           stream)
+    if PS != 0:
+        paged_attn_reduce(out.view(B, Lq * Hq, D), ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens,
+                          ws.max_context_len, PS, stream)
 
 
 def paged_attn_reduce(out: torch.Tensor, tmp_out: torch.Tensor, max_logits: torch.Tensor,

@@ -204,6 +204,7 @@ struct DecodeParams {
   float* max_logits;
   float* exp_sums;
   int B;
+  int L;           // query tokens per sequence (1 for decode); MFMA columns = G * L
   int max_blocks;
   int Hq;
   int Hkv;
@@ -435,10 +436,15 @@ void pa_decode_kernel(DecodeParams a) {
   }
 
   // ---- per-lane constants
-  const int hh = lane & 15;     // query head within the group (MFMA column)
+  // MFMA column hh = (query head hh / L of the group, new query token hh % L).  Token i of the
+  // L new tokens sits at position n - L + i and sees the first n - (L - 1 - i) tokens.
+  const int hh = lane & 15;
   const int grp = lane >> 4;    // MFMA row group
-  const bool hvalid = hh < a.G;
-  const int hoff = g * a.G + (hvalid ? hh : 0);
+  const bool hvalid = hh < a.G * a.L;
+  const int hsel = hvalid ? hh : 0;
+  const int qi = hsel % a.L;
+  const int hoff = g * a.G + hsel / a.L;
+  const int hidden = a.L - 1 - qi;                      // newer tokens this column must not see
   const int rowstride = a.Hkv * TL::ROWB;               // bytes between consecutive tokens
   int koff[TL::KLD];
 #pragma unroll
@@ -479,7 +485,7 @@ void pa_decode_kernel(DecodeParams a) {
   // of MFMA columns >= G load a valid head of the group: those columns are computed and
   // dropped, and no select on the loaded value forces a wait right after the loads.
   auto load_q = [&](int b, u32x4* qv) {
-    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + hoff) * D * 2;
+    const char* qrow = (const char*)a.q + (((size_t)b * a.L + qi) * a.Hq + hoff) * D * 2;
 #pragma unroll
     for (int s = 0; s < TL::NS; ++s) {
       int d0;
@@ -553,27 +559,33 @@ void pa_decode_kernel(DecodeParams a) {
     return s;
   };
 
-  // Second half: online softmax (exp2 domain) and O^T += V^T . P^T.  Tokens >= n are
-  // selected out of the scores and their V rows are zeroed (stale bytes may be NaN).
+  // Second half: online softmax (exp2 domain) and O^T += V^T . P^T.  Tokens a column may not
+  // see (>= n, or newer than its own query token) are selected out of the scores, and V rows
+  // >= n are zeroed (stale bytes may be NaN).  A column that has seen no token yet keeps
+  // m = -inf; its probabilities are computed against 0 so that they come out 0, not NaN.
   auto part2 = [&](int tile, int n, f32x4 s) {
     const int tbase = (tile << 4) + 4 * grp;
+    const int lim = n - hidden;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (tbase + e < n) ? s[e] * a.c2 : -INFINITY;
+    for (int e = 0; e < 4; ++e) x[e] = (tbase + e < lim) ? s[e] * a.c2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_rows32(max_rows16(mx));
     if (__ballot(mx > m) != 0) {
+      // every lane rescales when any column's maximum rises; a column that has seen no token
+      // yet (m = -inf, possible under the causal mask) has nothing to rescale
       const float mn = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
       lsum *= alpha;
 #pragma unroll
       for (int T = 0; T < TL::NT; ++T) acc[T] *= alpha;
     }
     unsigned short ph[4];
+    const float mb = m == -INFINITY ? 0.f : m;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[e] - m));
+      ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[e] - mb));
       lsum += from16<BF>(ph[e]);
     }
     const u32x2 pop = {pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
@@ -598,7 +610,7 @@ void pa_decode_kernel(DecodeParams a) {
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
     if (hvalid) {
       if constexpr (MODE == MODE_SINGLE) {
-        unsigned short* orow = (unsigned short*)a.out + ((size_t)sg.b * a.Hq + hoff) * D;
+        unsigned short* orow = (unsigned short*)a.out + (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * D;
 #pragma unroll
         for (int T = 0; T < TL::NT; ++T) {
           u32x2 wv;
@@ -607,7 +619,7 @@ void pa_decode_kernel(DecodeParams a) {
           *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
         }
       } else if (sg.slot >= 0 && sg.slot < a.Pslots) {
-        const size_t prow = ((size_t)sg.b * a.Hq + hoff) * a.Pslots + sg.slot;
+        const size_t prow = (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * a.Pslots + sg.slot;
         float* orow = a.tmp_out + prow * D;
 #pragma unroll
         for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
@@ -780,9 +792,10 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
       o[i + 2] = v[2];
       o[i + 3] = v[3];
     }
+    // a partial that saw no token (causal multi-query) has m = -inf and l = 0
     const float mn = fmaxf(mrun, mp);
-    const float so = __builtin_amdgcn_exp2f(mrun - mn);
-    const float sn = lp * __builtin_amdgcn_exp2f(mp - mn);
+    const float so = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float sn = mp == -INFINITY ? 0.f : lp * __builtin_amdgcn_exp2f(mp - mn);
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * so + o[i] * sn;
     wrun = wrun * so + sn;
@@ -791,8 +804,9 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
   // combine the four rows: rescale each to the common maximum (a row without partials has
   // mrun = -inf and weight 0), then sum across rows
   const float M = max_rows32(max_rows16(mrun));
-  const float sg = __builtin_amdgcn_exp2f(mrun - M);
-  const float inv = 1.0f / sum_rows32(sum_rows16(wrun * sg));
+  const float sg = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - M);
+  const float wsum = sum_rows32(sum_rows16(wrun * sg));
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = sum_rows32(sum_rows16(acc[i] * sg));
   if (grp == 0) {
@@ -988,17 +1002,19 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
   return launch_status();
 }
 
-int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+// Shared by paged_attn_decode (q_len 1) and paged_attn_multi_query.
+static int attn_entry(void* out, const void* query, const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
-                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                      int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
-                      float v_scale, int max_context_len, int partition_size, float* tmp_out,
-                      float* max_logits, float* exp_sums, void* stream) {
+                      int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
+                      float k_scale, float v_scale, int max_context_len, int partition_size,
+                      float* tmp_out, float* max_logits, float* exp_sums, void* stream) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks < 0 ||
-      max_context_len < 0 || partition_size < -(1 << 20))
+      max_context_len < 0 || partition_size < -(1 << 20) || q_len < 1 || q_len > 16)
     return PKV_ERR_SHAPE;
-  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16 || num_kv_heads > 16)
+  if (num_heads % num_kv_heads != 0 || (num_heads / num_kv_heads) * q_len > 16 || num_kv_heads > 16)
     return PKV_ERR_SHAPE;
+  if ((long long)num_seqs * q_len * num_heads >= (1LL << 31)) return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_SHAPE;
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0) return PKV_ERR_SHAPE;
   if (partition_size > 0 && (partition_size % block_size != 0)) return PKV_ERR_SHAPE;
@@ -1041,6 +1057,7 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
 
   DecodeParams p;
   p.B = num_seqs;
+  p.L = q_len;
   p.mode = partition_size == 0 ? MODE_SINGLE : (partition_size > 0 ? MODE_FIXED : MODE_BALANCED);
   p.W = partition_size < 0 ? -partition_size : 0;
   p.cap = (int)std::min<long long>(max_context_len, (long long)max_blocks * block_size);
@@ -1075,6 +1092,29 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
     else    { if (bf) launch_decode<64, KBF16, true>(p, st); else launch_decode<64, KF16, false>(p, st); }
   }
   return launch_status();
+}
+
+int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
+                      float v_scale, int max_context_len, int partition_size, float* tmp_out,
+                      float* max_logits, float* exp_sums, void* stream) {
+  return attn_entry(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens, num_seqs, 1,
+                    num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, q_dtype, kv_dtype,
+                    k_scale, v_scale, max_context_len, partition_size, tmp_out, max_logits, exp_sums, stream);
+}
+
+int paged_attn_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                           int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
+                           float k_scale, float v_scale, int max_context_len, int partition_size,
+                           float* tmp_out, float* max_logits, float* exp_sums, void* stream) {
+  return attn_entry(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens, num_seqs,
+                    q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, q_dtype,
+                    kv_dtype, k_scale, v_scale, max_context_len, partition_size, tmp_out, max_logits,
+                    exp_sums, stream);
 }
 
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,

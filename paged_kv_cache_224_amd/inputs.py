@@ -367,3 +367,10 @@ def algorithmic_bytes(w: Workload) -> Dict[str, int]:
     write = T * cfg.Hkv * cfg.D * 2 * (e_src + e_kv) + 8 * T
     return {"kv_logical": kv_logical, "kv_unique": kv_unique, "other": other,
             "decode_logical": kv_logical + other, "decode_unique": kv_unique + other, "write": write}
+
+
+def multi_query_q(cfg: Config, q_len: int, seed: int) -> torch.Tensor:
+    """Seeded queries [B, q_len, Hq, D] for L new tokens per sequence: N(0,1) drawn in fp32,
+    rounded to the query dtype (nearest even), like the decode query."""
+    gen = torch.Generator().manual_seed(10_000 + seed)
+    return _normals(gen, (cfg.B, q_len, cfg.Hq, cfg.D), DTYPES[cfg.q_dtype])

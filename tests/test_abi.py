@@ -30,6 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce", "paged_kv_copy_blocks",
+                          "paged_attn_multi_query",
                           "paged_kv_swap_blocks", "pkv_bm_create", "pkv_bm_append", "pkv_bm_check",
                           "paged_attn_workspace_bytes", "paged_attn_partial_slots",
                           "paged_attn_balanced_split", "pkv_status_string"}
@@ -91,6 +92,25 @@ def _decode(**kw):
 ])
 def test_decode_rejects(kw, want):
     assert _decode(**kw) == want
+
+
+def _mq(**kw):
+    args = dict(out=A, q=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, L=2, Hq=8, Hkv=2, D=64, BS=16,
+                NB=80, scale=0.125, qdt=0, kvdt=0, ks=1.0, vs=1.0, maxlen=256, PS=0, tmp=None, ml=None,
+                es=None, stream=None)
+    args.update(kw)
+    return pk.lib().paged_attn_multi_query(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(L=0), E_SHAPE),
+    (dict(L=5), E_SHAPE),                      # G = 4 query heads x 5 tokens > 16 MFMA columns
+    (dict(Hq=16, Hkv=1, L=2), E_SHAPE),        # 16 x 2 > 16
+    (dict(PS=-64), E_WS),
+    (dict(out=None), E_NULL),
+])
+def test_multi_query_rejects(kw, want):
+    assert _mq(**kw) == want
 
 
 def test_decode_zero_sequences_is_a_noop():
