@@ -46,10 +46,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per pool copy)")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "swap"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "swap", "multi_query"],
                     help="decode: the decode step (default); copy_blocks / swap: the whole-block operations "
                          "on a pool of the workload's block shape")
     ap.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks / swap call")
+    ap.add_argument("--q-len", type=int, default=4, help="new tokens per sequence for --op multi_query")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only copy a buffer of this size 5 times (reference for HBM traffic counters)")
     return ap.parse_args()
@@ -206,6 +207,86 @@ def block_ops(args):
     print(json.dumps(res), flush=True)
 
 
+def device_pools(w, dev, copies=None):
+    """Copies of the workload's pools on the device (fp8 pools quantised by paged_kv_write),
+    enough of them that a rotation over them never finds its pool in the 256 MB Infinity Cache."""
+    cfg = w.cfg
+    fp8 = cfg.kv_dtype == "fp8"
+    NB, BS, D = w.num_blocks, cfg.block_size, cfg.D
+    pool_bytes = 2 * NB * BS * cfg.Hkv * D * (1 if fp8 else 2)
+    copies = copies or max(2, math.ceil(1.5 * 2 ** 30 / pool_bytes) + 1)
+    pools = []
+    ksrc = w.k_pool.to(dev)
+    vsrc = w.v_pool.to(dev)
+    for _ in range(copies):
+        if fp8:
+            kc = torch.empty((NB, BS, cfg.Hkv, D), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+            slots = torch.arange(NB * BS, dtype=torch.int64, device=dev)
+            pk.paged_kv_write(ksrc.view(NB * BS, cfg.Hkv, D), vsrc.view(NB * BS, cfg.Hkv, D), kc, vc, slots,
+                              w.k_scale, w.v_scale)
+        else:
+            kc, vc = ksrc.clone(), vsrc.clone()
+        pools.append((kc, vc))
+    return pools, copies
+
+
+def multi_query_op(args):
+    """L new tokens per sequence (speculative verification / chunked prefill) on the workload's
+    batch: the multi-query kernel timed by HIP events, the whole call (kernel + reduce) by wall
+    clock.  Algorithmic bytes: the KV rows once (shared by the L tokens), L query rows and L
+    output rows per (sequence, head), the used table entries and lengths."""
+    dev = torch.device("cuda:0")
+    cfg = I.CONFIGS[args.workload]
+    L = args.q_len
+    w = I.make_workload(cfg)
+    fp8 = cfg.kv_dtype == "fp8"
+    pools, copies = device_pools(w, dev, args.copies)
+    q = I.multi_query_q(cfg, L, 0).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], torch.uint8 if fp8 else I.DTYPES[cfg.kv_dtype])
+    ws = pk.DecodeWorkspace(cfg.B, L * cfg.Hq, cfg.D, cfg.max_len, PS, device=dev)
+    out = torch.empty((cfg.B, L, cfg.Hq, cfg.D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def run(i, e=None):
+        kc, vc = pools[i % copies]
+        if e is not None:
+            e[0].record()
+        pk.paged_attn_multi_query(None, q, kc, vc, bt, lens, w.scale, cfg.max_len, PS, ws.tmp_out, ws.max_logits,
+                                  ws.exp_sums, w.k_scale, w.v_scale)
+        if e is not None:
+            e[1].record()
+        pk.paged_attn_reduce(out.view(cfg.B, L * cfg.Hq, cfg.D), ws.tmp_out, ws.max_logits, ws.exp_sums, lens,
+                             cfg.max_len, PS)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i, ev[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    nb = I.algorithmic_bytes(w)
+    e_q = 2
+    moved = nb["kv_unique"] + 2 * L * cfg.B * cfg.Hq * cfg.D * e_q + 4 * int(w.blocks_used.sum()) + 4 * cfg.B
+    gbps = moved / kern / 1e9
+    res = {"metric": "multi-query paged attention KV GB/s and query tokens/s", "value": round(gbps, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8" if fp8 else cfg.kv_dtype, "data": "synthetic",
+           "config": {"workload": cfg.name, "q_len": L, "num_seqs": cfg.B, "num_heads": cfg.Hq,
+                      "num_kv_heads": cfg.Hkv, "head_dim": cfg.D, "partition_size": PS},
+           "query_tokens_per_s": round(cfg.B * L / wall, 1), "kernel_ms_mean": round(kern * 1e3, 5),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_decode_kernel",
+                        "bytes_per_launch": moved}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -216,6 +297,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_reference:
         copy_reference(args.copy_reference)
+        return
+    if args.op == "multi_query":
+        multi_query_op(args)
         return
     if args.op != "decode":
         block_ops(args)
@@ -239,22 +323,7 @@ def main():
 
     # ---- device-resident inputs
     NB, BS = w.num_blocks, cfg.block_size
-    pool_bytes = 2 * NB * BS * cfg.Hkv * D * (1 if fp8 else 2)
-    copies = args.copies or max(2, math.ceil(1.5 * 2 ** 30 / pool_bytes) + 1)
-    pools = []
-    ksrc = w.k_pool.to(dev)
-    vsrc = w.v_pool.to(dev)
-    for _ in range(copies):
-        if fp8:
-            kc = torch.empty((NB, BS, cfg.Hkv, D), dtype=torch.uint8, device=dev)
-            vc = torch.empty_like(kc)
-            slots = torch.arange(NB * BS, dtype=torch.int64, device=dev)
-            pk.paged_kv_write(ksrc.view(NB * BS, cfg.Hkv, D), vsrc.view(NB * BS, cfg.Hkv, D), kc, vc, slots,
-                              w.k_scale, w.v_scale)
-        else:
-            kc, vc = ksrc.clone(), vsrc.clone()
-        pools.append((kc, vc))
-    del ksrc, vsrc
+    pools, copies = device_pools(w, dev, args.copies)
     q = w.q.to(dev)
     k_new, v_new = w.k_new.to(dev), w.v_new.to(dev)
     slots = torch.from_numpy(w.slot_mapping).to(dev)
