@@ -248,6 +248,7 @@ def multi_query_op(args):
     PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], torch.uint8 if fp8 else I.DTYPES[cfg.kv_dtype])
     ws = pk.DecodeWorkspace(cfg.B, L * cfg.Hq, cfg.D, cfg.max_len, PS, device=dev)
     out = torch.empty((cfg.B, L, cfg.Hq, cfg.D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
+    shared = bool(w.prefix_blocks.size)                 # tables share a common prefix's blocks
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
     def run(i, e=None):
@@ -255,7 +256,7 @@ def multi_query_op(args):
         if e is not None:
             e[0].record()
         pk.paged_attn_multi_query(None, q, kc, vc, bt, lens, w.scale, cfg.max_len, PS, ws.tmp_out, ws.max_logits,
-                                  ws.exp_sums, w.k_scale, w.v_scale)
+                                  ws.exp_sums, w.k_scale, w.v_scale, shared_blocks=shared)
         if e is not None:
             e[1].record()
         pk.paged_attn_reduce(out.view(cfg.B, L * cfg.Hq, cfg.D), ws.tmp_out, ws.max_logits, ws.exp_sums, lens,
@@ -332,6 +333,7 @@ def main():
     maxlen = cfg.max_len
     ws = pk.DecodeWorkspace(B, Hq, D, maxlen, PS, device=dev)
     out = torch.empty((B, Hq, D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
+    shared = bool(w.prefix_blocks.size)                 # tables share a common prefix's blocks
     torch.cuda.synchronize()
 
     def step(i, ev=None):
@@ -340,7 +342,7 @@ def main():
         if ev is not None:
             ev[0].record()
         pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS, ws.tmp_out,
-                             ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale)
+                             ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale, shared_blocks=shared)
         if ev is not None:
             ev[1].record()
         if PS != 0:
@@ -407,7 +409,7 @@ def main():
             "workload": cfg.name, "num_seqs": B, "num_heads": Hq, "num_kv_heads": cfg.Hkv, "head_dim": D,
             "block_size": BS, "context_lens": list(cfg.lens), "sum_context": int(w.context_lens.sum()),
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype, "schedule": schedule, "partition_size": PS,
-            "new_tokens": B,
+            "new_tokens": B, "kv_load_policy": "cached" if shared else "streaming",
             "num_blocks": NB, "pool_copies_rotated": copies,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

@@ -64,6 +64,16 @@ typedef enum {
   PKV_ERR_HOST = -11       /* a host buffer is not pinned, device-mapped memory of the needed size */
 } pkv_status;
 
+/* Flags of the attention calls. */
+enum {
+  /* Some physical blocks are named by several rows of the block table (copy-on-write sharing,
+     e.g. a common prefix).  K/V loads then use the default cache policy so that the other
+     readers find the shared blocks in the Infinity Cache.  Without it every K/V byte is
+     assumed to be read once per call and is loaded non-temporally (faster for private
+     blocks; correct either way). */
+  PKV_FLAG_SHARED_BLOCKS = 1
+};
+
 /*
  * paged_kv_write -- scatter this step's new K and V rows into the block pools.
  *
@@ -130,6 +140,7 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
  *                    [num_seqs, num_heads, Pslots, head_dim], max_logits and exp_sums fp32
  *                    [num_seqs, num_heads, Pslots].  paged_attn_reduce, called with the same
  *                    partition_size, then forms `out`.
+ *   flags            0 or PKV_FLAG_SHARED_BLOCKS (see the flag); any other bit is PKV_ERR_SHAPE.
  *   Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256; num_kv_heads <= 16;
  *   G <= 16; (q, kv) dtypes (F16, F16), (BF16, BF16), (BF16, FP8_E4M3), (F16, FP8_E4M3).
  *   Every context_lens[b] must be <= max_context_len and <= max_blocks * block_size.
@@ -142,7 +153,7 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
                       int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
                       float v_scale, int max_context_len, int partition_size, float* tmp_out,
-                      float* max_logits, float* exp_sums, void* stream);
+                      float* max_logits, float* exp_sums, int flags, void* stream);
 
 /*
  * paged_attn_multi_query -- q_len new query tokens per sequence against its paged KV cache,
@@ -168,7 +179,7 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                            int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
                            int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
                            float k_scale, float v_scale, int max_context_len, int partition_size,
-                           float* tmp_out, float* max_logits, float* exp_sums, void* stream);
+                           float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream);
 
 /*
  * paged_attn_reduce -- merge split-K partials by log-sum-exp weighting.

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_ERR_SHAPE = -2
+PKV_FLAG_SHARED_BLOCKS = 1
 _DT = {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3,
        torch.float8_e4m3fn: PKV_FP8_E4M3}
 
@@ -41,10 +42,10 @@ def lib() -> ctypes.CDLL:
         L.paged_kv_write.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, F, P]
         L.paged_kv_write.restype = I
         L.paged_attn_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, F, F, I, I, P, P,
-                                        P, P]
+                                        P, I, P]
         L.paged_attn_decode.restype = I
         L.paged_attn_multi_query.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, I, F, F, I, I, P, P,
-                                             P, P]
+                                             P, I, P]
         L.paged_attn_multi_query.restype = I
         L.paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         L.paged_attn_reduce.restype = I
@@ -146,8 +147,9 @@ def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cach
                       scale: float, max_context_len: int, partition_size: int = 0,
                       tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
                       exp_sums: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
-                      stream=None) -> None:
-    """Decode attention; see include/pagedkv.h.  partition_size > 0 writes split-K partials."""
+                      stream=None, shared_blocks: bool = False) -> None:
+    """Decode attention; see include/pagedkv.h.  partition_size != 0 writes split-K partials.
+    shared_blocks: some physical blocks appear in several table rows (keeps them cached)."""
     B, Hq, D = query.shape
     NB, BS, Hkv, D2 = key_cache.shape
     if D2 != D or value_cache.shape != key_cache.shape:
@@ -158,7 +160,8 @@ def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cach
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv,
                                  D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
                                  float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
-                                 _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _stream(stream))
+                                 _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+                                 PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
     _check("paged_attn_decode", rc)
 
 
@@ -167,7 +170,7 @@ def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key
                            scale: float, max_context_len: int, partition_size: int = 0,
                            tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
                            exp_sums: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
-                           stream=None) -> None:
+                           stream=None, shared_blocks: bool = False) -> None:
     """query [B, L, Hq, D]: L new tokens per sequence, causal among themselves (include/pagedkv.h)."""
     B, Lq, Hq, D = query.shape
     NB, BS, Hkv, D2 = key_cache.shape
@@ -179,12 +182,13 @@ def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key
                                       _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Lq, Hq,
                                       Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
                                       float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
-                                      _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _stream(stream))
+                                      _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+                                      PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
     _check("paged_attn_multi_query", rc)
 
 
 def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, context_lens, scale,
-                ws: "DecodeWorkspace", k_scale=1.0, v_scale=1.0, stream=None) -> None:
+                ws: "DecodeWorkspace", k_scale=1.0, v_scale=1.0, stream=None, shared_blocks: bool = False) -> None:
     """paged_attn_multi_query, then paged_attn_reduce over q_len * Hq rows when split-K.
 
     ws must be a DecodeWorkspace for (num_seqs, q_len * num_heads, ...)."""
@@ -192,7 +196,7 @@ def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, 
     B, Lq, Hq, D = query.shape
     paged_attn_multi_query(out if PS == 0 else None, query, key_cache, value_cache, block_tables, context_lens,
                            scale, ws.max_context_len, PS, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale, v_scale,
-                           stream)
+                           stream, shared_blocks)
     if PS != 0:
         paged_attn_reduce(out.view(B, Lq * Hq, D), ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens,
                           ws.max_context_len, PS, stream)
@@ -231,12 +235,12 @@ class DecodeWorkspace:
 
 
 def decode(out: torch.Tensor, query, key_cache, value_cache, block_tables, context_lens, scale,
-           ws: DecodeWorkspace, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+           ws: DecodeWorkspace, k_scale=1.0, v_scale=1.0, stream=None, shared_blocks: bool = False) -> None:
     """paged_attn_decode, followed by paged_attn_reduce when the workspace is split-K."""
     PS = ws.partition_size
     paged_attn_decode(out if PS == 0 else None, query, key_cache, value_cache, block_tables, context_lens,
                       scale, ws.max_context_len, PS, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale, v_scale,
-                      stream)
+                      stream, shared_blocks)
     if PS != 0:
         paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens, ws.max_context_len, PS,
                           stream)

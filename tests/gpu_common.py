@@ -57,13 +57,18 @@ def gpu_pools(w, write_step=True):
     return kc, vc
 
 
-def gpu_decode(w, kc, vc, partition_size, max_context_len=None):
+def gpu_decode(w, kc, vc, partition_size, max_context_len=None, shared_blocks=None):
+    """Decode through the C ABI.  shared_blocks defaults to whether the workload's tables share
+    physical blocks (a common prefix)."""
     cfg = w.cfg
     maxlen = int(max_context_len if max_context_len is not None else max(1, int(w.context_lens.max(initial=0))))
     out = torch.full((cfg.B, cfg.Hq, cfg.D), float("nan"), dtype=I.DTYPES[cfg.q_dtype], device=DEV)
     ws = pk.DecodeWorkspace(cfg.B, cfg.Hq, cfg.D, maxlen, partition_size, device=DEV)
+    if shared_blocks is None:
+        shared_blocks = bool(w.prefix_blocks.size)
     pk.decode(out, w.q.to(DEV), kc, vc, torch.from_numpy(w.block_tables).to(DEV),
-              torch.from_numpy(w.context_lens).to(DEV), w.scale, ws, w.k_scale, w.v_scale)
+              torch.from_numpy(w.context_lens).to(DEV), w.scale, ws, w.k_scale, w.v_scale,
+              shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()
 

@@ -63,7 +63,7 @@ def test_workspace_bytes():
 def _decode(**kw):
     args = dict(out=A, q=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, Hq=8, Hkv=2, D=64, BS=16,
                 NB=80, scale=0.125, qdt=0, kvdt=0, ks=1.0, vs=1.0, maxlen=256, PS=0, tmp=None, ml=None,
-                es=None, stream=None)
+                es=None, flags=0, stream=None)
     args.update(kw)
     return pk.lib().paged_attn_decode(*args.values())
 
@@ -89,6 +89,7 @@ def _decode(**kw):
     (dict(kc=MIS), E_ALIGN),
     (dict(B=-1), E_SHAPE),
     (dict(NB=0), E_SHAPE),
+    (dict(flags=2), E_SHAPE),                  # unknown flag bit
 ])
 def test_decode_rejects(kw, want):
     assert _decode(**kw) == want
@@ -97,7 +98,7 @@ def test_decode_rejects(kw, want):
 def _mq(**kw):
     args = dict(out=A, q=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, L=2, Hq=8, Hkv=2, D=64, BS=16,
                 NB=80, scale=0.125, qdt=0, kvdt=0, ks=1.0, vs=1.0, maxlen=256, PS=0, tmp=None, ml=None,
-                es=None, stream=None)
+                es=None, flags=0, stream=None)
     args.update(kw)
     return pk.lib().paged_attn_multi_query(*args.values())
 

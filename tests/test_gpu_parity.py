@@ -137,6 +137,20 @@ def test_shared_prefix_equals_private_copies_on_gpu():
 
 
 @pytest.mark.parametrize("case", SMALL, ids=_case_id)
+def test_load_policy_flag_changes_no_result(case):
+    """The shared-blocks flag only picks the cache policy of the K/V loads: both settings give
+    the same bits in every schedule."""
+    name, kw = case
+    _say(f"[policy] {name} {kw}")
+    w = _small(name, **kw)
+    kc, vc = gpu_pools(w)
+    for PS in (0, 512, -64):
+        a = gpu_decode(w, kc, vc, PS, shared_blocks=False)
+        b = gpu_decode(w, kc, vc, PS, shared_blocks=True)
+        assert np.array_equal(a, b, equal_nan=True), PS
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_case_id)
 def test_split_partials_match_oracle(case):
     name, kw = case
     _say(f"[partials] {name}")
