@@ -37,8 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b", choices=I.CONFIG_ORDER)
-    ap.add_argument("--schedule", default="balanced", choices=["balanced", "fixed", "single"],
-                    help="balanced split-K (default), fixed 512-token partitions, or single pass")
+    ap.add_argument("--schedule", default="balanced", choices=["balanced", "fixed", "single", "shared_prefix"],
+                    help="balanced split-K (default), fixed 512-token partitions, single pass, or the "
+                         "shared-prefix decode (prefix pass + balanced suffix + merge in one call)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="explicit partition_size (overrides --schedule; <0 = balanced over -N workgroups)")
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate over")
@@ -309,7 +310,7 @@ def main():
     cfg = I.CONFIGS[args.workload]
     if args.partition_size is not None:
         PS = args.partition_size
-    elif args.schedule == "balanced":
+    elif args.schedule in ("balanced", "shared_prefix"):
         PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype],
                                torch.uint8 if cfg.kv_dtype == "fp8" else I.DTYPES[cfg.kv_dtype])
     elif args.schedule == "fixed":
@@ -317,6 +318,9 @@ def main():
     else:
         PS = 0
     schedule = "single" if PS == 0 else ("fixed" if PS > 0 else "balanced")
+    cascade = args.schedule == "shared_prefix"
+    if cascade:
+        schedule = "shared_prefix" 
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     w = I.make_workload(cfg)
     B, Hq, D = cfg.B, cfg.Hq, cfg.D
@@ -334,6 +338,11 @@ def main():
     ws = pk.DecodeWorkspace(B, Hq, D, maxlen, PS, device=dev)
     out = torch.empty((B, Hq, D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
     shared = bool(w.prefix_blocks.size)                 # tables share a common prefix's blocks
+    prefix_len = int(w.prefix_blocks.size) * BS
+    if cascade:
+        # the prefix pass reads the shared blocks; the suffix pass streams private blocks
+        sws = pk.SharedPrefixWorkspace(B, Hq, cfg.Hkv, D, maxlen, prefix_len, PS, device=dev)
+        shared = False
     torch.cuda.synchronize()
 
     def step(i, ev=None):
@@ -341,6 +350,11 @@ def main():
         pk.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
         if ev is not None:
             ev[0].record()
+        if cascade:                                     # three kernels: prefix, suffix, merge
+            pk.decode_shared_prefix(out, q, kc, vc, bt, lens, w.scale, sws, w.k_scale, w.v_scale)
+            if ev is not None:
+                ev[1].record()
+            return
         pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS, ws.tmp_out,
                              ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale, shared_blocks=shared)
         if ev is not None:
@@ -410,6 +424,7 @@ def main():
             "block_size": BS, "context_lens": list(cfg.lens), "sum_context": int(w.context_lens.sum()),
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype, "schedule": schedule, "partition_size": PS,
             "new_tokens": B, "kv_load_policy": "cached" if shared else "streaming",
+            **({"prefix_len": prefix_len, "prefix_partition_size": sws.prefix_partition_size} if cascade else {}),
             "num_blocks": NB, "pool_copies_rotated": copies,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -425,7 +440,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(cfg.name, schedule),
-            "kernel": "pa_decode_kernel",
+            "kernel": ("pa_prefix_kernel + pa_decode_kernel + pa_reduce_kernel (one call, timed together)"
+                       if cascade else "pa_decode_kernel"),
             "bytes_per_launch": dec_unique,
         },
     }

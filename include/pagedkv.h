@@ -182,6 +182,49 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                            float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream);
 
 /*
+ * paged_attn_decode_shared_prefix -- paged_attn_decode for a batch whose rows begin with a
+ * common prefix held in shared blocks (copy-on-write sharing for prefix caching:
+ * "vllm-project-vllm -- L2", section 9 "Memory Management" and the prefix-caching row of the
+ * section 10 "Key Performance Mechanisms" table; "vLLM", its summary of prefix caching across
+ * requests with a common prompt prefix).  It computes the same `out` as paged_attn_decode
+ * (up to rounding order) but reads the prefix once per group of rows instead of once per row:
+ *   1. a prefix pass scores the prefix against every row's queries at once (a dense product on
+ *      the matrix cores) and writes one partial per (row, head, prefix partition);
+ *   2. the balanced split-K decode streams each row's tokens past the prefix;
+ *   3. the log-sum-exp merge of all partials writes `out`.
+ *
+ *   prefix_len             tokens of the shared prefix: >= 0, a multiple of block_size, and
+ *                          prefix_len / block_size <= max_blocks.  The prefix is read through
+ *                          row 0's first prefix_len / block_size table entries; every row b
+ *                          must name the same blocks in its entries j < ceil(min(n, prefix_len)
+ *                          / block_size).  Rows shorter than the prefix see their own n tokens.
+ *   prefix_partition_size  prefix tokens per partition of the prefix pass: a positive multiple
+ *                          of 16 (ignored when prefix_len == 0).
+ *                          paged_attn_prefix_split() gives one that fills the device.
+ *   partition_size         < 0: the balanced split of the suffix pass, as in paged_attn_decode
+ *                          (paged_attn_balanced_split()).  Other values are PKV_ERR_SHAPE.
+ *   tmp_out, max_logits,
+ *   exp_sums               workspace with Pslots = paged_attn_shared_prefix_slots(
+ *                          max_context_len, prefix_len, prefix_partition_size, partition_size)
+ *                          slots per (row, head): shapes as in paged_attn_decode.  Its contents
+ *                          on return are unspecified.
+ *   out                    [num_seqs, num_heads, head_dim], q_dtype; always written.
+ *   flags                  0 or PKV_FLAG_SHARED_BLOCKS, for the suffix pass (its blocks are
+ *                          normally private to their rows).
+ * Every other argument, the supported set and the error behaviour are those of
+ * paged_attn_decode.  Entries that break the sharing contract give an unspecified result (no
+ * out-of-bounds access); PKV_CHECK=1 validates it and returns PKV_ERR_CHECK.  Deterministic.
+ */
+int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables, int max_blocks,
+                                    const int32_t* context_lens, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                    float scale, int q_dtype, int kv_dtype, float k_scale, float v_scale,
+                                    int max_context_len, int prefix_len, int prefix_partition_size,
+                                    int partition_size, float* tmp_out, float* max_logits, float* exp_sums,
+                                    int flags, void* stream);
+
+/*
  * paged_attn_reduce -- merge split-K partials by log-sum-exp weighting.
  *
  * For every (b, h), with P the number of partials paged_attn_decode wrote for sequence b
@@ -296,6 +339,17 @@ size_t paged_attn_workspace_bytes(int num_seqs, int num_heads, int head_dim, int
    -(compute units x decode workgroups resident per unit) for this shape and dtype pair.
    Returns 0 if no device is available or the shape is unsupported.  Queries the device. */
 int paged_attn_balanced_split(int num_kv_heads, int head_dim, int q_dtype, int kv_dtype);
+
+/* Partial slots per (row, head) paged_attn_decode_shared_prefix needs: ceil(prefix_len /
+   prefix_partition_size) for the prefix plus the balanced split's slots for the
+   max(max_context_len - prefix_len, 0) tokens past it.  PKV_ERR_SHAPE for invalid arguments. */
+int paged_attn_shared_prefix_slots(int max_context_len, int prefix_len, int prefix_partition_size,
+                                   int partition_size);
+
+/* prefix_partition_size for paged_attn_decode_shared_prefix that gives the prefix pass about one
+   workgroup per compute unit of the current HIP device (a multiple of 64).
+   Returns 0 if no device is available or an argument is invalid.  Queries the device. */
+int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int prefix_len);
 
 /* Static English text for a pkv_status value. */
 const char* pkv_status_string(int status);

@@ -49,6 +49,13 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_multi_query.restype = I
         L.paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         L.paged_attn_reduce.restype = I
+        L.paged_attn_decode_shared_prefix.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, F, F, I, I,
+                                                      I, I, P, P, P, I, P]
+        L.paged_attn_decode_shared_prefix.restype = I
+        L.paged_attn_shared_prefix_slots.argtypes = [I, I, I, I]
+        L.paged_attn_shared_prefix_slots.restype = I
+        L.paged_attn_prefix_split.argtypes = [I, I, I, I]
+        L.paged_attn_prefix_split.restype = I
         L.paged_attn_workspace_bytes.argtypes = [I, I, I, I, I]
         L.paged_attn_workspace_bytes.restype = ctypes.c_size_t
         L.paged_attn_partial_slots.argtypes = [I, I]
@@ -200,6 +207,69 @@ def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, 
     if PS != 0:
         paged_attn_reduce(out.view(B, Lq * Hq, D), ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens,
                           ws.max_context_len, PS, stream)
+
+
+def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                                    value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                    context_lens: torch.Tensor, scale: float, max_context_len: int,
+                                    prefix_len: int, prefix_partition_size: int, partition_size: int,
+                                    tmp_out: torch.Tensor, max_logits: torch.Tensor, exp_sums: torch.Tensor,
+                                    k_scale: float = 1.0, v_scale: float = 1.0, stream=None,
+                                    shared_blocks: bool = False) -> None:
+    """Decode of a batch whose rows share their first prefix_len tokens' blocks: prefix pass,
+    suffix pass and merge in one call; writes out [B, Hq, D] (include/pagedkv.h)."""
+    B, Hq, D = query.shape
+    NB, BS, Hkv, D2 = key_cache.shape
+    if D2 != D or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    rc = lib().paged_attn_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
+        float(k_scale), float(v_scale), int(max_context_len), int(prefix_len), int(prefix_partition_size),
+        int(partition_size), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
+    _check("paged_attn_decode_shared_prefix", rc)
+
+
+def prefix_split(num_seqs: int, num_heads: int, num_kv_heads: int, prefix_len: int) -> int:
+    """prefix_partition_size that gives the prefix pass about one workgroup per compute unit."""
+    v = int(lib().paged_attn_prefix_split(num_seqs, num_heads, num_kv_heads, prefix_len))
+    if v <= 0:
+        raise PagedKVError("paged_attn_prefix_split", v, "no device / invalid arguments")
+    return v
+
+
+class SharedPrefixWorkspace:
+    """Partial buffers of paged_attn_decode_shared_prefix for a fixed shape and split."""
+
+    def __init__(self, num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, prefix_len, partition_size,
+                 prefix_partition_size=None, device="cuda"):
+        if prefix_partition_size is None:
+            prefix_partition_size = prefix_split(num_seqs, num_heads, num_kv_heads, prefix_len) if prefix_len else 64
+        self.max_context_len = max_context_len
+        self.prefix_len = prefix_len
+        self.partition_size = partition_size
+        self.prefix_partition_size = prefix_partition_size
+        P = int(lib().paged_attn_shared_prefix_slots(max_context_len, prefix_len, prefix_partition_size,
+                                                     partition_size))
+        if P < 0:
+            raise PagedKVError("paged_attn_shared_prefix_slots", P, "invalid arguments")
+        self.slots = P
+        P = max(P, 1)
+        self.tmp_out = torch.empty((num_seqs, num_heads, P, head_dim), dtype=torch.float32, device=device)
+        self.max_logits = torch.empty((num_seqs, num_heads, P), dtype=torch.float32, device=device)
+        self.exp_sums = torch.empty((num_seqs, num_heads, P), dtype=torch.float32, device=device)
+
+
+def decode_shared_prefix(out: torch.Tensor, query, key_cache, value_cache, block_tables, context_lens, scale,
+                         ws: SharedPrefixWorkspace, k_scale=1.0, v_scale=1.0, stream=None,
+                         shared_blocks: bool = False) -> None:
+    paged_attn_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                                    ws.max_context_len, ws.prefix_len, ws.prefix_partition_size,
+                                    ws.partition_size, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale, v_scale,
+                                    stream, shared_blocks)
 
 
 def paged_attn_reduce(out: torch.Tensor, tmp_out: torch.Tensor, max_logits: torch.Tensor,

@@ -224,6 +224,9 @@ struct DecodeParams {
   int Pslots;      // partial slots per (sequence, head) in the workspace
   int W;           // balanced: workgroups per head group
   int cap;         // context lengths are clamped to [0, cap]
+  int t0;          // balanced split: tiles skipped at the start of every sequence (a shared
+                   // prefix handled elsewhere); the stream holds tiles [t0, ceil(n / 16))
+  int slot0;       // partial slots below slot0 belong to someone else (the prefix pass)
   int tile_shift;  // log2(BS / 16)
   float c2;        // scale * k_scale * log2(e)
   float v_scale;
@@ -258,7 +261,11 @@ __device__ __forceinline__ int lds_slot(int t, int c) {
 }
 
 __device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
-__device__ __forceinline__ int tiles_of(int n, int cap) { return (clamp_len(n, cap) + 15) >> 4; }
+// Tiles of an n-token sequence past its first t0 tiles.
+__device__ __forceinline__ int tiles_after(int n, int t0) {
+  const int t = ((n + 15) >> 4) - t0;
+  return t > 0 ? t : 0;
+}
 
 // Balanced split of the batch's (sequence, tile) stream of N tiles into Weff contiguous
 // ranges whose sizes differ by at most one: the first `rem` ranges hold q+1 tiles, the rest
@@ -295,7 +302,7 @@ struct Seg {
 // sequence b0+k), so moving from one segment to the next is register work only; a workgroup
 // whose range runs past b0+63 refills the table.
 struct SegSource {
-  int mode, B, cap, w;
+  int mode, B, cap, w, t0;
   Split split;
   long long lo, hi;
   const int32_t* lens;
@@ -312,7 +319,7 @@ struct SegSource {
     b0 = b;
     base = start;
     n_v = n_lane;
-    const int t = (n_v + 15) >> 4;
+    const int t = tiles_after(n_v, t0);
     st_v = wave_incl_scan(t) - t;
     const long long s0 = start + st_v;
     vmask = __ballot(t > 0 && s0 < hi && s0 + t > lo);
@@ -326,11 +333,11 @@ struct SegSource {
     s.b = b0 + k;
     s.n = __builtin_amdgcn_readlane(n_v, k);
     s.start = base + __builtin_amdgcn_readlane(st_v, k);
-    const long long nt = (s.n + 15) >> 4;
+    const long long nt = tiles_after(s.n, t0);
     const long long a = lo > s.start ? lo : s.start;
     const long long e = hi < s.start + nt ? hi : s.start + nt;
-    s.tlo = (int)(a - s.start);
-    s.thi = (int)(e - s.start);
+    s.tlo = t0 + (int)(a - s.start);                    // tile numbers within the sequence
+    s.thi = t0 + (int)(e - s.start);
     s.slot = w - split.owner((int)s.start);
     s.valid = true;
     return s;
@@ -342,7 +349,7 @@ struct SegSource {
       if (m) return make_lane(__builtin_ctzll(m));
       // nothing left in this table: does the range continue past sequence b0+63?
       const int n63 = __builtin_amdgcn_readlane(n_v, 63);
-      const long long next_start = base + __builtin_amdgcn_readlane(st_v, 63) + ((n63 + 15) >> 4);
+      const long long next_start = base + __builtin_amdgcn_readlane(st_v, 63) + tiles_after(n63, t0);
       if (b0 + 64 >= B || next_start >= hi) {
         Seg r;
         r.valid = false;
@@ -388,6 +395,7 @@ void pa_decode_kernel(DecodeParams a) {
   src.cap = cap;
   src.lens = a.lens;
   src.w = 0;
+  src.t0 = MODE == MODE_BALANCED ? a.t0 : 0;
   src.split = Split(1, 1);
   src.lo = 0;
   src.hi = 0;
@@ -418,7 +426,7 @@ void pa_decode_kernel(DecodeParams a) {
       const int bb = lane * per + i;
       const int n = bb < B ? clamp_len(a.lens[bb], cap) : 0;
       if (i == 0) n_first = n;
-      run += (n + 15) >> 4;
+      run += tiles_after(n, src.t0);
     }
     const int incl = wave_incl_scan(run);               // inclusive scan over lanes
     const int N = __builtin_amdgcn_readlane(incl, 63);
@@ -626,8 +634,8 @@ void pa_decode_kernel(DecodeParams a) {
           wv.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
           *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
         }
-      } else if (sg.slot >= 0 && sg.slot < a.Pslots) {
-        const size_t prow = (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * a.Pslots + sg.slot;
+      } else if (sg.slot >= 0 && a.slot0 + sg.slot < a.Pslots) {
+        const size_t prow = (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * a.Pslots + a.slot0 + sg.slot;
         float* orow = a.tmp_out + prow * D;
 #pragma unroll
         for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
@@ -726,12 +734,276 @@ void pa_decode_kernel(DecodeParams a) {
   }
 }
 
+// ------------------------------------------------------------------ shared-prefix pass
+
+// When every row of a batch starts with the same prefix (blocks shared copy-on-write), the
+// decode above streams the prefix once per row.  This pass reads it once per workgroup and
+// scores it against many rows' queries together, which makes the prefix a dense contraction
+// on MFMA: for KV head g, S = Q_g . K_prefix^T over all B * G query rows of that head.  A
+// workgroup takes one KV head, 128 query columns (8 waves x 16 MFMA columns) and one
+// partition of the prefix.  64-token stages of K and V pass through LDS once for all 8 waves
+// (fp8 is widened to 16 bits on the way in), double-buffered so the next stage's loads fly
+// while the current one is computed.  Each wave runs the online softmax of its 16 columns;
+// QK^T and PV both use v_mfma_f32_16x16x32 (PV takes two 16-token sub-tiles per step).  The
+// result is one (m, l, o) partial per (row, head, prefix partition), merged with the suffix
+// partials by the reduce.
+
+constexpr int kPrefixWaves = 8;
+constexpr int kPrefixCols = 16 * kPrefixWaves;   // query columns per workgroup
+constexpr int kPrefixStage = 64;                 // tokens per LDS stage
+
+struct PrefixParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;      // the first entries of row 0 are the prefix's blocks
+  const int32_t* lens;
+  float* tmp_out;
+  float* max_logits;
+  float* exp_sums;
+  int B, Hq, Hkv, G, num_blocks, cap;
+  int bs_shift;           // log2(block_size)
+  int prefix_len;         // tokens of the shared prefix, a multiple of 16
+  int chunk;              // tokens per prefix partition, a multiple of 16
+  int Pslots;
+  float c2, v_scale;
+};
+
+template <int D, int KV>
+struct PrefixTile {
+  static constexpr int ESZ = (KV == KFP8) ? 1 : 2;
+  static constexpr int ROWB = D * ESZ;                          // source bytes per (token, head)
+  static constexpr int CPRS = ROWB / 16;                        // 16-byte source chunks per row
+  static constexpr int CPR = D / 8;                             // 16-byte chunks of a 16-bit row
+  static constexpr int NCH = kPrefixStage * CPRS;               // source chunks per stage and pool
+  static constexpr int NLD = (NCH + 64 * kPrefixWaves - 1) / (64 * kPrefixWaves);
+  static constexpr int KST = kPrefixStage * D * 2;              // one pool's stage in LDS
+  static constexpr int SUB = 16 * D * 2;                        // a 16-token sub-tile
+  static constexpr int STAGE = 2 * KST;                         // K, then V
+  static constexpr int LDS_BYTES = 2 * STAGE;                   // double-buffered: 64 KiB at D = 128
+  static constexpr int NS = D / 32;
+  static constexpr int NT = D / 16;
+};
+
+// K rows in LDS: chunk c of row t sits at c ^ swizzle(t), so the 16 rows that one MFMA
+// A-operand read touches (16 lanes, same logical chunk) land in 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int kslot(int t, int c) {
+  const int swz = (CPR == 16) ? (t & 15) : ((t >> 1) & 7);
+  return t * CPR + (c ^ swz);
+}
+
+template <int D, int KV, bool BF>
+__global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixParams a) {
+  using PT = PrefixTile<D, KV>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int grp = lane >> 4;
+  const int wl = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.y;                                   // KV head
+  const int c0 = blockIdx.z * a.chunk;                        // the partition: tokens [c0, c1)
+  const int c1 = min(c0 + a.chunk, a.prefix_len);
+  const int nst = (c1 - c0 + kPrefixStage - 1) / kPrefixStage;
+  const int rowstride = a.Hkv * PT::ROWB;
+  const size_t blockbytes = (size_t)rowstride << a.bs_shift;
+  const int bsm1 = (1 << a.bs_shift) - 1;
+  const unsigned nbm1 = (unsigned)(a.num_blocks - 1);
+
+  // ---- stages: thread tid moves source chunks tid, tid + 512, ... of K and of V.  Rows past
+  // the partition's end are zero in LDS.  The block ids of a stage's rows (row 0 of the table)
+  // are loaded one stage before its K/V rows, so the row loads never wait on them.
+  u32x4 kreg[PT::NLD], vreg[PT::NLD];
+  int idn[PT::NLD];
+  auto load_ids = [&](int tok0) {
+#pragma unroll
+    for (int k = 0; k < PT::NLD; ++k) {
+      const int ci = tid + k * 64 * kPrefixWaves;
+      const int tok = tok0 + ci / PT::CPRS;
+      idn[k] = (ci < PT::NCH && tok < c1) ? a.bt[tok >> a.bs_shift] : 0;
+    }
+  };
+  auto load_stage = [&](int tok0) {
+#pragma unroll
+    for (int k = 0; k < PT::NLD; ++k) {
+      const int ci = tid + k * 64 * kPrefixWaves;
+      const int t = ci / PT::CPRS, cs = ci % PT::CPRS;
+      const int tok = tok0 + t;
+      kreg[k] = u32x4{0u, 0u, 0u, 0u};
+      vreg[k] = u32x4{0u, 0u, 0u, 0u};
+      if (ci < PT::NCH && tok < c1) {
+        const unsigned id = min((unsigned)idn[k], nbm1);
+        const size_t off = (size_t)id * blockbytes + (size_t)(tok & bsm1) * rowstride +
+                           (size_t)g * PT::ROWB + (size_t)cs * 16;
+        kreg[k] = *(const u32x4*)((const char*)a.kc + off);
+        vreg[k] = *(const u32x4*)((const char*)a.vc + off);
+      }
+    }
+  };
+  auto store_stage = [&](char* st) {
+#pragma unroll
+    for (int k = 0; k < PT::NLD; ++k) {
+      const int ci = tid + k * 64 * kPrefixWaves;
+      if (ci >= PT::NCH) continue;
+      const int t = ci / PT::CPRS, cs = ci % PT::CPRS;
+      char* vst = st + PT::KST + (t >> 4) * PT::SUB;
+      if constexpr (KV == KFP8) {
+        u32x4 lo, hi;
+        fp8x16_to_16<BF>(kreg[k], lo, hi);
+        *(u32x4*)(st + kslot<PT::CPR>(t, 2 * cs) * 16) = lo;
+        *(u32x4*)(st + kslot<PT::CPR>(t, 2 * cs + 1) * 16) = hi;
+        fp8x16_to_16<BF>(vreg[k], lo, hi);
+        *(u32x4*)(vst + lds_slot<PT::CPR>(t & 15, 2 * cs) * 16) = lo;
+        *(u32x4*)(vst + lds_slot<PT::CPR>(t & 15, 2 * cs + 1) * 16) = hi;
+      } else {
+        *(u32x4*)(st + kslot<PT::CPR>(t, cs) * 16) = kreg[k];
+        *(u32x4*)(vst + lds_slot<PT::CPR>(t & 15, cs) * 16) = vreg[k];
+      }
+    }
+  };
+  load_ids(c0);
+  load_stage(c0);
+  load_ids(c0 + kPrefixStage);
+
+  // ---- this wave's 16 query columns: column c is (sequence c / G, head g * G + c % G).
+  // Column c sees the first min(n, prefix_len) tokens of the prefix; inside this partition,
+  // the tokens below lim (the zero rows past the partition's end are not tokens).
+  const int BG = a.B * a.G;
+  const int cb = blockIdx.x * kPrefixCols + wl * 16;
+  const bool active = cb < BG;                                // wave-uniform
+  const int col = cb + (lane & 15);
+  const bool cvalid = col < BG;
+  const int cc = cvalid ? col : BG - 1;
+  const int b = cc / a.G;
+  const int head = g * a.G + (cc - b * a.G);
+  const int lim = cvalid ? min(min(clamp_len(a.lens[b], a.cap), a.prefix_len), c1) : 0;
+  // V rows at or past every column's limit are masked: no column of the wave may see them,
+  // and such slots of shared blocks may hold stale bytes
+  int wlim = lim;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) wlim = max(wlim, __shfl_xor(wlim, o));
+  wlim = __builtin_amdgcn_readfirstlane(wlim);
+  u32x4 qv[PT::NS];
+  {
+    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + head) * D * 2;
+#pragma unroll
+    for (int s = 0; s < PT::NS; ++s) qv[s] = *(const u32x4*)(qrow + (32 * s + 8 * grp) * 2);
+  }
+  int koff[PT::NS];
+#pragma unroll
+  for (int s = 0; s < PT::NS; ++s) koff[s] = kslot<PT::CPR>(lane & 15, 4 * s + grp) * 16;
+  int troff[PT::NT];
+  {
+    const int tt = 4 * grp + ((lane >> 2) & 3);
+    const int qq = lane & 3;
+#pragma unroll
+    for (int T = 0; T < PT::NT; ++T)
+      troff[T] = lds_slot<PT::CPR>(tt, 2 * T + (qq >> 1)) * 16 + (qq & 1) * 8;
+  }
+  f32x4 acc[PT::NT];
+#pragma unroll
+  for (int T = 0; T < PT::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  // One stage for the wave's columns: S^T of four 16-token sub-tiles, one softmax update over
+  // all 64 tokens, then O^T += V^T . P^T two sub-tiles at a time.
+  auto compute = [&](const char* st, int tok0) {
+    f32x4 sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < PT::NS; ++s)
+        sc[u] = mfma_16x16x32<BF>(*(const u32x4*)(st + u * PT::SUB + koff[s]), qv[s], sc[u]);
+    }
+    float x[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[u][e] = (tok0 + 16 * u + 4 * grp + e < lim) ? sc[u][e] * a.c2 : -INFINITY;
+        mx = fmaxf(mx, x[u][e]);
+      }
+    mx = max_rows32(max_rows16(mx));
+    if (__ballot(mx > m) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int T = 0; T < PT::NT; ++T) acc[T] *= alpha;
+    }
+    const float mb = m == -INFINITY ? 0.f : m;
+    u32x2 pop[4];
+    u32x2 vm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      unsigned short ph[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[u][e] - mb));
+        lsum += from16<BF>(ph[e]);
+      }
+      pop[u] = u32x2{pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
+      vm[u] = u32x2{0xffffffffu, 0xffffffffu};
+      const int tb = tok0 + 16 * u + 4 * grp;
+      if (wlim - (tok0 + 16 * u) < 16) {
+        vm[u].x = ((tb + 0 < wlim) ? 0x0000ffffu : 0u) | ((tb + 1 < wlim) ? 0xffff0000u : 0u);
+        vm[u].y = ((tb + 2 < wlim) ? 0x0000ffffu : 0u) | ((tb + 3 < wlim) ? 0xffff0000u : 0u);
+      }
+    }
+    const char* vst = st + PT::KST;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 pb = {pop[2 * h].x, pop[2 * h].y, pop[2 * h + 1].x, pop[2 * h + 1].y};
+#pragma unroll
+      for (int T = 0; T < PT::NT; ++T) {
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((lds_char*)(vst + (2 * h) * PT::SUB) + troff[T])));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((lds_char*)(vst + (2 * h + 1) * PT::SUB) + troff[T])));
+        const u32x4 va = {lo.x & vm[2 * h].x, lo.y & vm[2 * h].y, hi.x & vm[2 * h + 1].x, hi.y & vm[2 * h + 1].y};
+        acc[T] = mfma_16x16x32<BF>(va, pb, acc[T]);
+      }
+    }
+  };
+
+  store_stage(smem);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const bool more = s + 1 < nst;                              // uniform over the workgroup
+    if (more) {
+      load_stage(c0 + (s + 1) * kPrefixStage);
+      load_ids(c0 + (s + 2) * kPrefixStage);
+    }
+    if (active) compute(smem + (s & 1) * PT::STAGE, c0 + s * kPrefixStage);
+    if (more) store_stage(smem + ((s + 1) & 1) * PT::STAGE);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  const float l = sum_rows32(sum_rows16(lsum));
+  const float inv = l > 0.f ? a.v_scale / l : 0.f;
+  if (cvalid) {
+    const size_t prow = ((size_t)b * a.Hq + head) * a.Pslots + blockIdx.z;
+    float* orow = a.tmp_out + prow * D;
+#pragma unroll
+    for (int T = 0; T < PT::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
+    if (grp == 0) {
+      a.max_logits[prow] = m * kLn2;
+      a.exp_sums[prow] = l;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ split-K reduce
 
 // One wave per output row (sequence b, query head h); four rows per workgroup.  PS > 0:
 // partials of fixed partitions, P = ceil(n / PS).  PS < 0: balanced split over -PS
-// workgroups; P = number of ranges the sequence's tiles fall in, recomputed from the lengths
-// exactly as the decode did.  No LDS and no barrier: 16-lane row r of the wave folds the
+// workgroups; P = number of ranges the sequence's tiles (past its first t0) fall in,
+// recomputed from the lengths exactly as the decode did.  slot0 leading slots (a shared
+// prefix's partials) come before those P.  No LDS and no barrier: 16-lane row r of the wave folds the
 // partials p = r, r+4, ... into a running (max, weight sum, weighted o) over its D/16 output
 // elements per lane, and the four rows are combined with permlane swaps.
 template <int D, bool BF>
@@ -739,7 +1011,8 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
                                                        const float* max_logits,
                                                        const float* exp_sums,
                                                        const int32_t* lens, int B, int Hq,
-                                                       int Pslots, int PS, int cap) {
+                                                       int Pslots, int PS, int cap, int t0,
+                                                       int slot0) {
   constexpr int DPL = D / 16;                 // output elements per lane (8 or 4)
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, l16 = lane & 15;
@@ -754,13 +1027,13 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
     int total = 0, before = 0;               // tiles of the whole batch, of sequences < b
     for (int i0 = 0; i0 < B; i0 += 64) {
       const int i = i0 + lane;
-      const int t = i < B ? tiles_of(lens[i], cap) : 0;
+      const int t = i < B ? tiles_after(clamp_len(lens[i], cap), t0) : 0;
       total += t;
       before += i < b ? t : 0;
     }
     total = __builtin_amdgcn_readlane(wave_incl_scan(total), 63);
     before = __builtin_amdgcn_readlane(wave_incl_scan(before), 63);
-    const int nt = (n + 15) >> 4;
+    const int nt = tiles_after(n, t0);
     if (nt == 0) {
       P = 0;
     } else {
@@ -768,7 +1041,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
       P = split.owner(before + nt - 1) - split.owner(before) + 1;
     }
   }
-  P = min(P, Pslots);
+  P = min(slot0 + P, Pslots);
   unsigned short* orow = (unsigned short*)out + (size_t)row * D + l16 * DPL;
   if (P == 0) {
     if (grp == 0) {
@@ -909,6 +1182,37 @@ void launch_decode(const DecodeParams& p, bool shared_blocks, hipStream_t st) {
 }
 
 template <int D, int KV, bool BF>
+void launch_prefix(const PrefixParams& p, int parts, hipStream_t st) {
+  const dim3 grid((unsigned)((p.B * p.G + kPrefixCols - 1) / kPrefixCols), (unsigned)p.Hkv, (unsigned)parts);
+  const size_t lds = (size_t)PrefixTile<D, KV>::LDS_BYTES;
+  hipLaunchKernelGGL((pa_prefix_kernel<D, KV, BF>), grid, dim3(64 * kPrefixWaves), lds, st, p);
+}
+
+void launch_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
+                   const int32_t* lens, int B, int rows_per_seq, int D, int Pslots, int PS, int cap,
+                   int t0, int slot0, bool bf, hipStream_t st) {
+  const dim3 grid((unsigned)(((long long)B * rows_per_seq + 3) / 4)), block(256);
+  const int Pm = Pslots > 0 ? Pslots : 1;
+  if (D == 128) {
+    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
+    else    hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
+  } else {
+    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
+    else    hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
+  }
+}
+
+// Partial slots of a shared-prefix decode: the prefix partitions first, then the balanced
+// split of the suffix (the tokens past the prefix).
+int prefix_parts(int prefix_len, int prefix_partition_size) {
+  return prefix_len > 0 ? (prefix_len + prefix_partition_size - 1) / prefix_partition_size : 0;
+}
+int shared_prefix_slots(int max_context_len, int prefix_len, int prefix_partition_size, int partition_size) {
+  const int suffix = max_context_len > prefix_len ? max_context_len - prefix_len : 0;
+  return prefix_parts(prefix_len, prefix_partition_size) + slots_of(suffix, partition_size);
+}
+
+template <int D, int KV, bool BF>
 int occupancy_blocks(int Hkv) {
   int nb = 0;
   const int nw = waves_per_group(Hkv);
@@ -1019,18 +1323,18 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
   return launch_status();
 }
 
-// Shared by paged_attn_decode (q_len 1) and paged_attn_multi_query.
-static int attn_entry(void* out, const void* query, const void* key_cache, const void* value_cache,
+// Argument checks shared by the attention entry points.  Returns PKV_OK, an error, or 1 when
+// there is nothing to do (no sequences).
+static int check_attn(void* out, const void* query, const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
                       int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
                       float k_scale, float v_scale, int max_context_len, int partition_size,
-                      float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream) {
+                      float* tmp_out, float* max_logits, float* exp_sums, int flags) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks < 0 ||
       max_context_len < 0 || partition_size < -(1 << 20) || q_len < 1 || q_len > 16)
     return PKV_ERR_SHAPE;
   if ((flags & ~PKV_FLAG_SHARED_BLOCKS) != 0) return PKV_ERR_SHAPE;
-  const bool sh = (flags & PKV_FLAG_SHARED_BLOCKS) != 0;
   if (num_heads % num_kv_heads != 0 || (num_heads / num_kv_heads) * q_len > 16 || num_kv_heads > 16)
     return PKV_ERR_SHAPE;
   if ((long long)num_seqs * q_len * num_heads >= (1LL << 31)) return PKV_ERR_SHAPE;
@@ -1043,7 +1347,7 @@ static int attn_entry(void* out, const void* query, const void* key_cache, const
     return PKV_ERR_SHAPE;
   if (kv_dtype != PKV_FP8_E4M3 && (k_scale != 1.0f || v_scale != 1.0f)) return PKV_ERR_SHAPE;
   if ((long long)max_blocks * block_size > (1LL << 30)) return PKV_ERR_SHAPE;
-  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs == 0) return 1;
   if (!query || !key_cache || !value_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
   if (num_blocks == 0 || max_blocks == 0) return PKV_ERR_SHAPE;
   if (partition_size == 0 && !out) return PKV_ERR_NULL;
@@ -1053,27 +1357,42 @@ static int attn_entry(void* out, const void* query, const void* key_cache, const
       (tmp_out && !aligned(tmp_out, 16)) || (max_logits && !aligned(max_logits, 4)) ||
       (exp_sums && !aligned(exp_sums, 4)))
     return PKV_ERR_ALIGN;
-  const int Pslots = slots_of(max_context_len, partition_size);
-  if (partition_size != 0 && Pslots == 0) return PKV_OK;   // every context is empty
-  if (partition_size > 0 && Pslots > 65535) return PKV_ERR_SHAPE;
   if ((long long)num_seqs * ((max_context_len + 15) / 16) >= (1LL << 31)) return PKV_ERR_SHAPE;
-  hipStream_t st = (hipStream_t)stream;
+  return PKV_OK;
+}
 
-  if (check_mode()) {
-    std::vector<int32_t> lens, bt;
-    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, st)) return PKV_ERR_LAUNCH;
-    if (!copy_to_host(bt, block_tables, (size_t)num_seqs * max_blocks, st)) return PKV_ERR_LAUNCH;
-    for (int b = 0; b < num_seqs; ++b) {
-      const int n = lens[b];
-      if (n < 0 || n > max_context_len || (long long)n > (long long)max_blocks * block_size)
-        return PKV_ERR_CHECK;
-      for (int j = 0; j < (n + block_size - 1) / block_size; ++j) {
-        const int id = bt[(size_t)b * max_blocks + j];
-        if (id < 0 || id >= num_blocks) return PKV_ERR_CHECK;
-      }
+// Checked mode (PKV_CHECK=1): lengths within bounds and every table entry a sequence uses
+// inside the pool; with prefix_len > 0 also the shared prefix: the entries covering the first
+// min(n, prefix_len) tokens of every row equal row 0's.
+static int check_tables(const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                        int num_seqs, int block_size, int num_blocks, int max_context_len,
+                        int prefix_len, hipStream_t st) {
+  std::vector<int32_t> lens, bt;
+  if (!copy_to_host(lens, context_lens, (size_t)num_seqs, st)) return PKV_ERR_LAUNCH;
+  if (!copy_to_host(bt, block_tables, (size_t)num_seqs * max_blocks, st)) return PKV_ERR_LAUNCH;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int n = lens[b];
+    if (n < 0 || n > max_context_len || (long long)n > (long long)max_blocks * block_size)
+      return PKV_ERR_CHECK;
+    for (int j = 0; j < (n + block_size - 1) / block_size; ++j) {
+      const int id = bt[(size_t)b * max_blocks + j];
+      if (id < 0 || id >= num_blocks) return PKV_ERR_CHECK;
     }
+    const int shared = (std::min(n, prefix_len) + block_size - 1) / block_size;
+    for (int j = 0; j < shared; ++j)
+      if (bt[(size_t)b * max_blocks + j] != bt[j]) return PKV_ERR_CHECK;
   }
+  for (int j = 0; j < prefix_len / block_size; ++j)
+    if (bt[j] < 0 || bt[j] >= num_blocks) return PKV_ERR_CHECK;
+  return PKV_OK;
+}
 
+static DecodeParams make_params(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                                int num_seqs, int q_len, int num_heads, int num_kv_heads, int block_size,
+                                int num_blocks, float scale, float k_scale, float v_scale, int max_context_len,
+                                int partition_size, int Pslots, float* tmp_out, float* max_logits,
+                                float* exp_sums) {
   DecodeParams p;
   p.B = num_seqs;
   p.L = q_len;
@@ -1100,7 +1419,13 @@ static int attn_entry(void* out, const void* query, const void* key_cache, const
   p.tile_shift = __builtin_ctz((unsigned)block_size) - 4;
   p.c2 = scale * k_scale * kLog2e;
   p.v_scale = v_scale;
+  p.t0 = 0;
+  p.slot0 = 0;
+  return p;
+}
 
+static void launch_decode_dt(const DecodeParams& p, int head_dim, int q_dtype, int kv_dtype, bool sh,
+                             hipStream_t st) {
   const bool bf = q_dtype == PKV_BF16;
   const bool f8 = kv_dtype == PKV_FP8_E4M3;
   if (head_dim == 128) {
@@ -1110,6 +1435,34 @@ static int attn_entry(void* out, const void* query, const void* key_cache, const
     if (f8) { if (bf) launch_decode<64, KFP8, true>(p, sh, st); else launch_decode<64, KFP8, false>(p, sh, st); }
     else    { if (bf) launch_decode<64, KBF16, true>(p, sh, st); else launch_decode<64, KF16, false>(p, sh, st); }
   }
+}
+
+// Shared by paged_attn_decode (q_len 1) and paged_attn_multi_query.
+static int attn_entry(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                      int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
+                      float k_scale, float v_scale, int max_context_len, int partition_size,
+                      float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream) {
+  const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                            num_seqs, q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                            q_dtype, kv_dtype, k_scale, v_scale, max_context_len, partition_size, tmp_out,
+                            max_logits, exp_sums, flags);
+  if (rc != PKV_OK) return rc > 0 ? PKV_OK : rc;
+  const int Pslots = slots_of(max_context_len, partition_size);
+  if (partition_size != 0 && Pslots == 0) return PKV_OK;   // every context is empty
+  if (partition_size > 0 && Pslots > 65535) return PKV_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (check_mode()) {
+    const int cr = check_tables(block_tables, max_blocks, context_lens, num_seqs, block_size, num_blocks,
+                                max_context_len, 0, st);
+    if (cr != PKV_OK) return cr;
+  }
+  const DecodeParams p = make_params(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                                     num_seqs, q_len, num_heads, num_kv_heads, block_size, num_blocks, scale,
+                                     k_scale, v_scale, max_context_len, partition_size, Pslots, tmp_out,
+                                     max_logits, exp_sums);
+  launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, st);
   return launch_status();
 }
 
@@ -1137,6 +1490,100 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                     exp_sums, flags, stream);
 }
 
+int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables, int max_blocks,
+                                    const int32_t* context_lens, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                    float scale, int q_dtype, int kv_dtype, float k_scale, float v_scale,
+                                    int max_context_len, int prefix_len, int prefix_partition_size,
+                                    int partition_size, float* tmp_out, float* max_logits, float* exp_sums,
+                                    int flags, void* stream) {
+  if (partition_size >= 0) return PKV_ERR_SHAPE;              // the suffix runs the balanced split
+  const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                            num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                            q_dtype, kv_dtype, k_scale, v_scale, max_context_len, partition_size, tmp_out,
+                            max_logits, exp_sums, flags);
+  if (rc != PKV_OK) return rc > 0 ? PKV_OK : rc;
+  if (!out) return PKV_ERR_NULL;
+  if (prefix_len < 0 || prefix_len % block_size != 0 || (long long)prefix_len > (long long)max_blocks * block_size)
+    return PKV_ERR_SHAPE;
+  if (prefix_len > 0 && (prefix_partition_size < 16 || prefix_partition_size % 16 != 0))
+    return PKV_ERR_SHAPE;
+  const int parts = prefix_parts(prefix_len, prefix_partition_size);
+  const int Pslots = shared_prefix_slots(max_context_len, prefix_len, prefix_partition_size, partition_size);
+  if (Pslots > 65535) return PKV_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (check_mode()) {
+    const int cr = check_tables(block_tables, max_blocks, context_lens, num_seqs, block_size, num_blocks,
+                                max_context_len, prefix_len, st);
+    if (cr != PKV_OK) return cr;
+  }
+  DecodeParams p = make_params(nullptr, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                               num_seqs, 1, num_heads, num_kv_heads, block_size, num_blocks, scale, k_scale,
+                               v_scale, max_context_len, partition_size, Pslots, tmp_out, max_logits, exp_sums);
+  p.t0 = prefix_len / 16;
+  p.slot0 = parts;
+  const bool bf = q_dtype == PKV_BF16;
+  const bool f8 = kv_dtype == PKV_FP8_E4M3;
+  if (parts > 0) {
+    PrefixParams pp;
+    pp.q = query;
+    pp.kc = key_cache;
+    pp.vc = value_cache;
+    pp.bt = block_tables;
+    pp.lens = context_lens;
+    pp.tmp_out = tmp_out;
+    pp.max_logits = max_logits;
+    pp.exp_sums = exp_sums;
+    pp.B = num_seqs;
+    pp.Hq = num_heads;
+    pp.Hkv = num_kv_heads;
+    pp.G = num_heads / num_kv_heads;
+    pp.num_blocks = num_blocks;
+    pp.cap = p.cap;
+    pp.bs_shift = __builtin_ctz((unsigned)block_size);
+    pp.prefix_len = prefix_len;
+    pp.chunk = prefix_partition_size;
+    pp.Pslots = Pslots;
+    pp.c2 = p.c2;
+    pp.v_scale = v_scale;
+    if (head_dim == 128) {
+      if (f8) { if (bf) launch_prefix<128, KFP8, true>(pp, parts, st); else launch_prefix<128, KFP8, false>(pp, parts, st); }
+      else    { if (bf) launch_prefix<128, KBF16, true>(pp, parts, st); else launch_prefix<128, KF16, false>(pp, parts, st); }
+    } else {
+      if (f8) { if (bf) launch_prefix<64, KFP8, true>(pp, parts, st); else launch_prefix<64, KFP8, false>(pp, parts, st); }
+      else    { if (bf) launch_prefix<64, KBF16, true>(pp, parts, st); else launch_prefix<64, KF16, false>(pp, parts, st); }
+    }
+  }
+  if (Pslots > parts) launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, st);
+  launch_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, head_dim, Pslots,
+                partition_size, p.cap, p.t0, parts, bf, st);
+  return launch_status();
+}
+
+int paged_attn_shared_prefix_slots(int max_context_len, int prefix_len, int prefix_partition_size,
+                                   int partition_size) {
+  if (max_context_len < 0 || prefix_len < 0 || partition_size >= 0 ||
+      (prefix_len > 0 && prefix_partition_size <= 0))
+    return PKV_ERR_SHAPE;
+  return shared_prefix_slots(max_context_len, prefix_len, prefix_partition_size, partition_size);
+}
+
+int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int prefix_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || prefix_len <= 0)
+    return 0;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  const long long cols = (long long)num_seqs * (num_heads / num_kv_heads);
+  const long long units = (cols + kPrefixCols - 1) / kPrefixCols * num_kv_heads;
+  long long parts = (prop.multiProcessorCount + units - 1) / units;
+  if (parts < 1) parts = 1;
+  long long size = (prefix_len + parts - 1) / parts;
+  size = (size + kPrefixStage - 1) / kPrefixStage * kPrefixStage;
+  return (int)size;
+}
+
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                       int max_context_len, int partition_size, int out_dtype, void* stream) {
@@ -1159,16 +1606,8 @@ int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, 
     for (int n : lens)
       if (n < 0 || n > max_context_len) return PKV_ERR_CHECK;
   }
-  dim3 grid((unsigned)(((long long)num_seqs * num_heads + 3) / 4)), block(256);
-  const int Pm = Pslots > 0 ? Pslots : 1;
-  const bool bf = out_dtype == PKV_BF16;
-  if (head_dim == 128) {
-    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
-    else    hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
-  } else {
-    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
-    else    hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, Pm, partition_size, max_context_len);
-  }
+  launch_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, head_dim, Pslots,
+                partition_size, max_context_len, 0, 0, out_dtype == PKV_BF16, st);
   return launch_status();
 }
 

@@ -30,7 +30,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce", "paged_kv_copy_blocks",
-                          "paged_attn_multi_query",
+                          "paged_attn_multi_query", "paged_attn_decode_shared_prefix",
+                          "paged_attn_shared_prefix_slots", "paged_attn_prefix_split",
                           "paged_kv_swap_blocks", "pkv_bm_create", "pkv_bm_append", "pkv_bm_check",
                           "paged_attn_workspace_bytes", "paged_attn_partial_slots",
                           "paged_attn_balanced_split", "pkv_status_string"}
@@ -112,6 +113,52 @@ def _mq(**kw):
 ])
 def test_multi_query_rejects(kw, want):
     assert _mq(**kw) == want
+
+
+def _sp(**kw):
+    args = dict(out=A, q=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, Hq=8, Hkv=2, D=64, BS=16,
+                NB=80, scale=0.125, qdt=0, kvdt=0, ks=1.0, vs=1.0, maxlen=256, P=128, PP=64, PS=-64, tmp=A,
+                ml=A, es=A, flags=0, stream=None)
+    args.update(kw)
+    return pk.lib().paged_attn_decode_shared_prefix(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(PS=0), E_SHAPE),                     # the suffix pass is the balanced split
+    (dict(PS=512), E_SHAPE),
+    (dict(P=-16), E_SHAPE),
+    (dict(P=24), E_SHAPE),                     # not a multiple of block_size
+    (dict(P=272), E_SHAPE),                    # 17 blocks > max_blocks
+    (dict(PP=0), E_SHAPE),
+    (dict(PP=40), E_SHAPE),                    # not a multiple of 16
+    (dict(out=None), E_NULL),                  # the merged output is always written
+    (dict(tmp=None), E_WS),
+    (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(D=96), E_SHAPE),
+    (dict(qdt=0, kvdt=1), E_DTYPE),
+    (dict(q=MIS), E_ALIGN),
+    (dict(flags=4), E_SHAPE),
+])
+def test_shared_prefix_rejects(kw, want):
+    assert _sp(**kw) == want
+
+
+def test_shared_prefix_slots():
+    L = pk.lib()
+    # prefix partitions first, then the balanced split's slots for the tokens past the prefix
+    assert L.paged_attn_shared_prefix_slots(2560, 2048, 512, -256) == 4 + (32 // 8 + 1)
+    assert L.paged_attn_shared_prefix_slots(2560, 2048, 100, -256) == 21 + 5
+    assert L.paged_attn_shared_prefix_slots(2048, 2048, 512, -256) == 4
+    assert L.paged_attn_shared_prefix_slots(100, 0, 0, -8) == L.paged_attn_partial_slots(100, -8)
+    assert L.paged_attn_shared_prefix_slots(0, 0, 0, -8) == 0
+    assert L.paged_attn_shared_prefix_slots(100, 64, 0, -8) == E_SHAPE
+    assert L.paged_attn_shared_prefix_slots(100, 0, 64, 512) == E_SHAPE
+    assert L.paged_attn_prefix_split(0, 32, 8, 2048) == 0            # invalid: no device query
+    assert L.paged_attn_prefix_split(4, 32, 8, 0) == 0
+
+
+def test_shared_prefix_zero_sequences_is_a_noop():
+    assert _sp(B=0, q=None, out=None) == OK
 
 
 def test_decode_zero_sequences_is_a_noop():
