@@ -42,6 +42,8 @@ def parse():
                          "shared-prefix decode (prefix pass + balanced suffix + merge in one call)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="explicit partition_size (overrides --schedule; <0 = balanced over -N workgroups)")
+    ap.add_argument("--prefix-partition-size", type=int, default=None,
+                    help="shared_prefix schedule: prefix tokens per partition (default: one workgroup per CU)")
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
@@ -341,7 +343,8 @@ def main():
     prefix_len = int(w.prefix_blocks.size) * BS
     if cascade:
         # the prefix pass reads the shared blocks; the suffix pass streams private blocks
-        sws = pk.SharedPrefixWorkspace(B, Hq, cfg.Hkv, D, maxlen, prefix_len, PS, device=dev)
+        sws = pk.SharedPrefixWorkspace(B, Hq, cfg.Hkv, D, maxlen, prefix_len, PS, args.prefix_partition_size,
+                                       device=dev)
         shared = False
     torch.cuda.synchronize()
 

@@ -37,6 +37,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "pagedkv.h"
@@ -135,6 +136,20 @@ __device__ __forceinline__ float from16(unsigned short h) {
 
 __device__ __forceinline__ unsigned pack2(unsigned short lo, unsigned short hi) {
   return (unsigned)lo | ((unsigned)hi << 16);
+}
+
+// Two floats -> two 16-bit values (round to nearest even) packed lo | hi << 16, one
+// v_cvt_pk_bf16_f32 for bf16.
+template <bool BF>
+__device__ __forceinline__ unsigned pack2_16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (BF) {
+    typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, b16x2));
+  } else {
+    typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, h16x2));
+  }
 }
 
 // OCP E4M3FN code of y, nearest-even, saturating at +-448 (written from the format: bias 7,
@@ -765,6 +780,8 @@ struct PrefixParams {
   int bs_shift;           // log2(block_size)
   int prefix_len;         // tokens of the shared prefix, a multiple of 16
   int chunk;              // tokens per prefix partition, a multiple of 16
+  int parts;              // prefix partitions
+  int hp8;                // Hkv * parts rounded up to a multiple of 8 (the grid's stride)
   int Pslots;
   float c2, v_scale;
 };
@@ -801,8 +818,15 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
   const int lane = tid & 63;
   const int grp = lane >> 4;
   const int wl = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = blockIdx.y;                                   // KV head
-  const int c0 = blockIdx.z * a.chunk;                        // the partition: tokens [c0, c1)
+  // Workgroup w = hc + hp8 * qb: (KV head, partition) hc, query block qb.  Workgroups are dealt
+  // to the 8 XCDs round-robin by w, so all query blocks of one (head, partition) land on the
+  // same XCD and read its slice of the prefix through one L2.
+  const int hc = blockIdx.x % a.hp8;
+  const int qb = blockIdx.x / a.hp8;
+  if (hc >= a.Hkv * a.parts) return;                          // padding of the stride
+  const int g = hc % a.Hkv;                                   // KV head
+  const int part = hc / a.Hkv;
+  const int c0 = part * a.chunk;                              // the partition: tokens [c0, c1)
   const int c1 = min(c0 + a.chunk, a.prefix_len);
   const int nst = (c1 - c0 + kPrefixStage - 1) / kPrefixStage;
   const int rowstride = a.Hkv * PT::ROWB;
@@ -869,7 +893,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
   // Column c sees the first min(n, prefix_len) tokens of the prefix; inside this partition,
   // the tokens below lim (the zero rows past the partition's end are not tokens).
   const int BG = a.B * a.G;
-  const int cb = blockIdx.x * kPrefixCols + wl * 16;
+  const int cb = qb * kPrefixCols + wl * 16;
   const bool active = cb < BG;                                // wave-uniform
   const int col = cb + (lane & 15);
   const bool cvalid = col < BG;
@@ -903,11 +927,26 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
   f32x4 acc[PT::NT];
 #pragma unroll
   for (int T = 0; T < PT::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  float m = -INFINITY;
+
+  // P^T row sums (the softmax denominators) come from the matrix cores: an A operand of
+  // bf16/f16 ones against the same P^T tile adds sum_t p to every row of accL, so the running
+  // sum is rescaled with the output and needs no cross-lane reduction.
+  const unsigned one2 = BF ? 0x3f803f80u : 0x3c003c00u;
+  const u32x4 ones = {one2, one2, one2, one2};
+  f32x4 accL = {0.f, 0.f, 0.f, 0.f};
+  // Columns of the wave that see every token of a stage need no masks: the lowest limit.
+  int wmin = lim;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) wmin = min(wmin, __shfl_xor(wmin, o));
+  wmin = __builtin_amdgcn_readfirstlane(wmin);
 
   // One stage for the wave's columns: S^T of four 16-token sub-tiles, one softmax update over
-  // all 64 tokens, then O^T += V^T . P^T two sub-tiles at a time.
-  auto compute = [&](const char* st, int tok0) {
+  // all 64 tokens, then O^T += V^T . P^T two sub-tiles at a time.  MASKED: some column of the
+  // wave stops inside the stage (per-column select on the scores, zeroed V rows past every
+  // column's limit); otherwise the exponent is one fma per score.
+  auto compute = [&](const char* st, int tok0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     f32x4 sc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -917,76 +956,126 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
         sc[u] = mfma_16x16x32<BF>(*(const u32x4*)(st + u * PT::SUB + koff[s]), qv[s], sc[u]);
     }
     float x[4][4];
-    float mx = -INFINITY;
+    float mx;
+    if constexpr (MASKED) {
+      mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[u][e] = (tok0 + 16 * u + 4 * grp + e < lim) ? sc[u][e] * a.c2 : -INFINITY;
-        mx = fmaxf(mx, x[u][e]);
+        for (int e = 0; e < 4; ++e) {
+          x[u][e] = (tok0 + 16 * u + 4 * grp + e < lim) ? sc[u][e] * a.c2 : -INFINITY;
+          mx = fmaxf(mx, x[u][e]);
+        }
+    } else {
+      // max of c2 * s over the stage = c2 * (max s, or min s for a negative scale)
+      float r = sc[0][0];
+      if (a.c2 >= 0.f) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r = fmaxf(r, sc[u][e]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r = fminf(r, sc[u][e]);
       }
+      mx = r * a.c2;
+    }
     mx = max_rows32(max_rows16(mx));
     if (__ballot(mx > m) != 0) {
       const float mn = fmaxf(m, mx);
       const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
-      lsum *= alpha;
+      accL *= alpha;
 #pragma unroll
       for (int T = 0; T < PT::NT; ++T) acc[T] *= alpha;
     }
     const float mb = m == -INFINITY ? 0.f : m;
     u32x2 pop[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pr[e] = __builtin_amdgcn_exp2f(MASKED ? x[u][e] - mb : __builtin_fmaf(sc[u][e], a.c2, -mb));
+      pop[u] = u32x2{pack2_16<BF>(pr[0], pr[1]), pack2_16<BF>(pr[2], pr[3])};
+    }
     u32x2 vm[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      unsigned short ph[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[u][e] - mb));
-        lsum += from16<BF>(ph[e]);
-      }
-      pop[u] = u32x2{pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
       vm[u] = u32x2{0xffffffffu, 0xffffffffu};
-      const int tb = tok0 + 16 * u + 4 * grp;
-      if (wlim - (tok0 + 16 * u) < 16) {
-        vm[u].x = ((tb + 0 < wlim) ? 0x0000ffffu : 0u) | ((tb + 1 < wlim) ? 0xffff0000u : 0u);
-        vm[u].y = ((tb + 2 < wlim) ? 0x0000ffffu : 0u) | ((tb + 3 < wlim) ? 0xffff0000u : 0u);
+      if constexpr (MASKED) {
+        const int tb = tok0 + 16 * u + 4 * grp;
+        if (wlim - (tok0 + 16 * u) < 16) {
+          vm[u].x = ((tb + 0 < wlim) ? 0x0000ffffu : 0u) | ((tb + 1 < wlim) ? 0xffff0000u : 0u);
+          vm[u].y = ((tb + 2 < wlim) ? 0x0000ffffu : 0u) | ((tb + 3 < wlim) ? 0xffff0000u : 0u);
+        }
       }
     }
     const char* vst = st + PT::KST;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const u32x4 pb = {pop[2 * h].x, pop[2 * h].y, pop[2 * h + 1].x, pop[2 * h + 1].y};
+      accL = mfma_16x16x32<BF>(ones, pb, accL);
 #pragma unroll
       for (int T = 0; T < PT::NT; ++T) {
         const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)((lds_char*)(vst + (2 * h) * PT::SUB) + troff[T])));
         const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)((lds_char*)(vst + (2 * h + 1) * PT::SUB) + troff[T])));
-        const u32x4 va = {lo.x & vm[2 * h].x, lo.y & vm[2 * h].y, hi.x & vm[2 * h + 1].x, hi.y & vm[2 * h + 1].y};
+        u32x4 va;
+        if constexpr (MASKED)
+          va = u32x4{lo.x & vm[2 * h].x, lo.y & vm[2 * h].y, hi.x & vm[2 * h + 1].x, hi.y & vm[2 * h + 1].y};
+        else
+          va = u32x4{lo.x, lo.y, hi.x, hi.y};
         acc[T] = mfma_16x16x32<BF>(va, pb, acc[T]);
       }
     }
   };
 
   store_stage(smem);
+  // q must be resident before the loop: loads retire in order, so a q load still counted as
+  // outstanding inside the loop would make the first MFMA wait for the next stage's prefetch.
+#pragma unroll
+  for (int s = 0; s < PT::NS; ++s) asm volatile("" : : "v"(qv[s]));
   __syncthreads();
-  for (int s = 0; s < nst; ++s) {
+  // Stage s: prefetch stage s + 1 into registers, compute stage s from LDS buffer s & 1, store
+  // stage s + 1 into the other buffer, one barrier.  Every wave passes the same barriers.
+  auto stage = [&](int s, char* cur, char* nxt, auto masked_tag) {
     const bool more = s + 1 < nst;                              // uniform over the workgroup
     if (more) {
       load_stage(c0 + (s + 1) * kPrefixStage);
       load_ids(c0 + (s + 2) * kPrefixStage);
     }
-    if (active) compute(smem + (s & 1) * PT::STAGE, c0 + s * kPrefixStage);
-    if (more) store_stage(smem + ((s + 1) & 1) * PT::STAGE);
+    if (active) compute(cur, c0 + s * kPrefixStage, masked_tag);
+    if (more) store_stage(nxt);
     __syncthreads();
+  };
+  // The stages every column of this wave sees whole come first and need no masks; they run
+  // unrolled by two so the LDS buffer offsets are immediates.  The rest (usually the last
+  // stage or none) runs the masked compute.  Keeping the two apart also keeps the
+  // accumulators in place instead of merging two paths every stage.
+  int nfast = active ? (wmin - c0) / kPrefixStage : 0;
+  nfast = nfast < 0 ? 0 : (nfast > nst ? nst : nfast);
+  char* const buf0 = smem;
+  char* const buf1 = smem + PT::STAGE;
+  int s = 0;
+  for (; s + 2 <= nfast; s += 2) {
+    stage(s, buf0, buf1, std::false_type{});
+    stage(s + 1, buf1, buf0, std::false_type{});
   }
+  if (s < nfast) {
+    stage(s, buf0, buf1, std::false_type{});
+    ++s;
+  }
+  for (; s < nst; ++s) stage(s, (s & 1) ? buf1 : buf0, (s & 1) ? buf0 : buf1, std::true_type{});
 
   if (!active) return;
-  const float l = sum_rows32(sum_rows16(lsum));
+  const float l = accL[0];
   const float inv = l > 0.f ? a.v_scale / l : 0.f;
   if (cvalid) {
-    const size_t prow = ((size_t)b * a.Hq + head) * a.Pslots + blockIdx.z;
+    const size_t prow = ((size_t)b * a.Hq + head) * a.Pslots + part;
     float* orow = a.tmp_out + prow * D;
 #pragma unroll
     for (int T = 0; T < PT::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
@@ -1182,8 +1271,9 @@ void launch_decode(const DecodeParams& p, bool shared_blocks, hipStream_t st) {
 }
 
 template <int D, int KV, bool BF>
-void launch_prefix(const PrefixParams& p, int parts, hipStream_t st) {
-  const dim3 grid((unsigned)((p.B * p.G + kPrefixCols - 1) / kPrefixCols), (unsigned)p.Hkv, (unsigned)parts);
+void launch_prefix(const PrefixParams& p, hipStream_t st) {
+  const long long qblocks = ((long long)p.B * p.G + kPrefixCols - 1) / kPrefixCols;
+  const dim3 grid((unsigned)(qblocks * p.hp8));
   const size_t lds = (size_t)PrefixTile<D, KV>::LDS_BYTES;
   hipLaunchKernelGGL((pa_prefix_kernel<D, KV, BF>), grid, dim3(64 * kPrefixWaves), lds, st, p);
 }
@@ -1512,6 +1602,9 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
   const int parts = prefix_parts(prefix_len, prefix_partition_size);
   const int Pslots = shared_prefix_slots(max_context_len, prefix_len, prefix_partition_size, partition_size);
   if (Pslots > 65535) return PKV_ERR_SHAPE;
+  const long long prefix_groups = ((long long)num_seqs * (num_heads / num_kv_heads) + kPrefixCols - 1) /
+                                  kPrefixCols * ((num_kv_heads * (long long)parts + 7) / 8 * 8);
+  if (prefix_groups >= (1LL << 31)) return PKV_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
   if (check_mode()) {
     const int cr = check_tables(block_tables, max_blocks, context_lens, num_seqs, block_size, num_blocks,
@@ -1544,15 +1637,17 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
     pp.bs_shift = __builtin_ctz((unsigned)block_size);
     pp.prefix_len = prefix_len;
     pp.chunk = prefix_partition_size;
+    pp.parts = parts;
+    pp.hp8 = (num_kv_heads * parts + 7) / 8 * 8;
     pp.Pslots = Pslots;
     pp.c2 = p.c2;
     pp.v_scale = v_scale;
     if (head_dim == 128) {
-      if (f8) { if (bf) launch_prefix<128, KFP8, true>(pp, parts, st); else launch_prefix<128, KFP8, false>(pp, parts, st); }
-      else    { if (bf) launch_prefix<128, KBF16, true>(pp, parts, st); else launch_prefix<128, KF16, false>(pp, parts, st); }
+      if (f8) { if (bf) launch_prefix<128, KFP8, true>(pp, st); else launch_prefix<128, KFP8, false>(pp, st); }
+      else    { if (bf) launch_prefix<128, KBF16, true>(pp, st); else launch_prefix<128, KF16, false>(pp, st); }
     } else {
-      if (f8) { if (bf) launch_prefix<64, KFP8, true>(pp, parts, st); else launch_prefix<64, KFP8, false>(pp, parts, st); }
-      else    { if (bf) launch_prefix<64, KBF16, true>(pp, parts, st); else launch_prefix<64, KF16, false>(pp, parts, st); }
+      if (f8) { if (bf) launch_prefix<64, KFP8, true>(pp, st); else launch_prefix<64, KFP8, false>(pp, st); }
+      else    { if (bf) launch_prefix<64, KBF16, true>(pp, st); else launch_prefix<64, KF16, false>(pp, st); }
     }
   }
   if (Pslots > parts) launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, st);
