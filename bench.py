@@ -46,6 +46,9 @@ def parse():
                     help="shared_prefix schedule: prefix tokens per partition (default: one workgroup per CU)")
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append", action="store_true",
+                    help="16-bit caches, balanced schedule: run the step's KV write inside the decode launch "
+                         "(paged_attn_decode_append) instead of paged_kv_write + paged_attn_decode")
     ap.add_argument("--event-every", type=int, default=5,
                     help="bracket the decode launch with HIP events on every N-th timed step (1 = all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
@@ -343,6 +346,8 @@ def main():
     out = torch.empty((B, Hq, D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
     shared = bool(w.prefix_blocks.size)                 # tables share a common prefix's blocks
     prefix_len = int(w.prefix_blocks.size) * BS
+    # --append (16-bit caches, balanced schedule): the step's KV write rides in the decode launch
+    append = args.append and not fp8 and schedule == "balanced" and args.partition_size is None
     if cascade:
         # the prefix pass reads the shared blocks; the suffix pass streams private blocks
         sws = pk.SharedPrefixWorkspace(B, Hq, cfg.Hkv, D, maxlen, prefix_len, PS, args.prefix_partition_size,
@@ -352,6 +357,15 @@ def main():
 
     def step(i, ev=None):
         kc, vc = pools[i % copies]
+        if append:                                      # write + decode in one launch, then the merge
+            if ev is not None:
+                ev[0].record()
+            pk.paged_attn_decode_append(None, q, k_new, v_new, kc, vc, bt, lens, w.scale, maxlen, PS, ws.tmp_out,
+                                        ws.max_logits, ws.exp_sums, shared_blocks=shared)
+            if ev is not None:
+                ev[1].record()
+            pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS)
+            return
         pk.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
         if ev is not None:
             ev[0].record()
@@ -413,6 +427,8 @@ def main():
     step_bytes_logical = nb["decode_logical"] + nb["write"]
     value = step_bytes_unique / (ms_per_step * 1e-3) / 1e9
     dec_mean_ms = float(np.mean(decode_ms))
+    if append:                                          # the timed launch also moves the new rows
+        dec_unique += nb["write"]
     achieved = dec_unique / (dec_mean_ms * 1e-3) / 1e9
     tokens_per_s = B / (ms_per_step * 1e-3)
 
@@ -434,6 +450,7 @@ def main():
             "block_size": BS, "context_lens": list(cfg.lens), "sum_context": int(w.context_lens.sum()),
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype, "schedule": schedule, "partition_size": PS,
             "new_tokens": B, "kv_load_policy": "cached" if shared else "streaming",
+            "kv_write": "in the decode launch" if append else "separate launch",
             **({"prefix_len": prefix_len, "prefix_partition_size": sws.prefix_partition_size} if cascade else {}),
             "num_blocks": NB, "pool_copies_rotated": copies,
         },
@@ -452,7 +469,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(cfg.name, schedule),
             "kernel": ("pa_prefix_kernel + pa_decode_kernel + pa_reduce_kernel (one call, timed together)"
-                       if cascade else "pa_decode_kernel"),
+                       if cascade else ("pa_decode_kernel with the step's KV write appended" if append
+                                        else "pa_decode_kernel")),
             "bytes_per_launch": dec_unique,
         },
     }

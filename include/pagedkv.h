@@ -182,6 +182,35 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                            float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream);
 
 /*
+ * paged_attn_decode_append -- one decode step in one call for 16-bit caches: the step's new
+ * token of every sequence is stored in the pool and attended to, as paged_kv_write followed by
+ * paged_attn_decode would do (blocks are extended every decode step: "vllm-project-vllm -- L2",
+ * section 6 "KV Cache Block Tables"; section 7 on decode).
+ *
+ * For every b with n = context_lens[b] >= 1 the new token sits at position n - 1: key[b] and
+ * value[b] ([num_seqs, num_kv_heads, head_dim], dtype) are stored at slot
+ * block_tables[b][(n-1) / block_size] * block_size + (n-1) % block_size of the pools -- the
+ * bytes paged_kv_write would store with that slot_mapping -- and the attention over the n
+ * tokens (the new one included) is computed exactly as paged_attn_decode computes it, with the
+ * same partials and the same bits.  Sequences with n = 0 store nothing and give a zero row.
+ * The caller must have made that block private to sequence b (copy-on-write), as for
+ * paged_kv_write.
+ *   dtype           PKV_F16 or PKV_BF16: the query, the new rows and both pools.
+ *   partition_size  < 0 (balanced split): the rows are stored by the decode launch itself (the
+ *                   wave that streams the tile of position n - 1 uses the new row in place of
+ *                   the pool's and stores it).  >= 0: a scatter launch, then the decode.
+ * Every other argument, the supported set and the error behaviour are those of
+ * paged_attn_decode (k_scale = v_scale = 1).  An fp8 cache is PKV_ERR_DTYPE (use
+ * paged_kv_write and paged_attn_decode).
+ */
+int paged_attn_decode_append(void* out, const void* query, const void* key, const void* value,
+                             void* key_cache, void* value_cache, const int32_t* block_tables, int max_blocks,
+                             const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, float scale, int dtype,
+                             int max_context_len, int partition_size, float* tmp_out, float* max_logits,
+                             float* exp_sums, int flags, void* stream);
+
+/*
  * paged_attn_decode_shared_prefix -- paged_attn_decode for a batch whose rows begin with a
  * common prefix held in shared blocks (copy-on-write sharing for prefix caching:
  * "vllm-project-vllm -- L2", section 9 "Memory Management" and the prefix-caching row of the

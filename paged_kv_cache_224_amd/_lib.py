@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_multi_query.restype = I
         L.paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         L.paged_attn_reduce.restype = I
+        L.paged_attn_decode_append.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, I, P, P, P,
+                                               I, P]
+        L.paged_attn_decode_append.restype = I
         L.paged_attn_decode_shared_prefix.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, F, F, I, I,
                                                       I, I, P, P, P, I, P]
         L.paged_attn_decode_shared_prefix.restype = I
@@ -207,6 +210,41 @@ def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, 
     if PS != 0:
         paged_attn_reduce(out.view(B, Lq * Hq, D), ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens,
                           ws.max_context_len, PS, stream)
+
+
+def paged_attn_decode_append(out: Optional[torch.Tensor], query: torch.Tensor, key: torch.Tensor,
+                             value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                             max_context_len: int, partition_size: int = 0,
+                             tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
+                             exp_sums: Optional[torch.Tensor] = None, stream=None,
+                             shared_blocks: bool = False) -> None:
+    """Store key/value [B, Hkv, D] at position n - 1 of every sequence and decode, in one call
+    (16-bit caches; include/pagedkv.h).  partition_size != 0 writes split-K partials."""
+    B, Hq, D = query.shape
+    NB, BS, Hkv, D2 = key_cache.shape
+    if D2 != D or value_cache.shape != key_cache.shape or key.shape != (B, Hkv, D) or value.shape != key.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    rc = lib().paged_attn_decode_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype],
+        int(max_context_len), int(partition_size), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
+    _check("paged_attn_decode_append", rc)
+
+
+def decode_append(out: torch.Tensor, query, key, value, key_cache, value_cache, block_tables, context_lens, scale,
+                  ws: "DecodeWorkspace", stream=None, shared_blocks: bool = False) -> None:
+    """paged_attn_decode_append, followed by paged_attn_reduce when the workspace is split-K."""
+    PS = ws.partition_size
+    paged_attn_decode_append(out if PS == 0 else None, query, key, value, key_cache, value_cache, block_tables,
+                             context_lens, scale, ws.max_context_len, PS, ws.tmp_out, ws.max_logits, ws.exp_sums,
+                             stream, shared_blocks)
+    if PS != 0:
+        paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens, ws.max_context_len, PS,
+                          stream)
 
 
 def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

@@ -226,6 +226,8 @@ struct DecodeParams {
   float* tmp_out;
   float* max_logits;
   float* exp_sums;
+  const void* knew;  // append: the step's new K rows [B, Hkv, D], stored at position n - 1
+  const void* vnew;  // append: the new V rows
   int B;
   int L;           // query tokens per sequence (1 for decode); MFMA columns = G * L
   int max_blocks;
@@ -390,10 +392,16 @@ struct SegSource {
 // Every load result is first read at least one tile after it was issued, and nothing waits
 // on a value right after loading it, so the in-order load counter never drains the tile
 // in flight.
-template <int D, int KV, bool BF, int MODE, int POLICY>
+//
+// APPEND (16-bit caches): the step's new token of every sequence is not in the pool yet.  The
+// wave that streams the tile holding position n - 1 fetches the new K/V row of its head
+// together with that tile's loads, uses it in place of the stale pool row and stores it into
+// the pool; no other workgroup reads that slot during the launch.
+template <int D, int KV, bool BF, int MODE, int POLICY, bool APPEND = false>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_decode_kernel(DecodeParams a) {
   using TL = Tile<D, KV>;
+  static_assert(!APPEND || (KV != KFP8 && TL::PF == 1), "append is for 16-bit caches, one tile in flight");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -689,8 +697,31 @@ void pa_decode_kernel(DecodeParams a) {
   // Load the tile at the issue position, then advance it and fetch the next block id (past
   // the stream's end the last tile is loaded again: an L2 hit that keeps every load
   // unconditional).
+  // Append state of the tile in flight: whether it holds the new token, the token's row in the
+  // tile, the pool offset of that row (head g), and the new row's values for the lanes that
+  // hold it in the A operand (K) and in the V load pattern.
+  bool apn = false;
+  int aprow = 0;
+  size_t apoff = 0;
+  u32x4 knew[APPEND ? TL::KLD : 1], vnew;
   auto issue = [&](u32x4* kd, u32x4* vd) {
-    load_tile((unsigned)__builtin_amdgcn_readfirstlane(nid), itile, kd, vd);
+    const unsigned id = (unsigned)__builtin_amdgcn_readfirstlane(nid);
+    load_tile(id, itile, kd, vd);
+    if constexpr (APPEND) {
+      apn = !idone && itile == ((iseg.n - 1) >> 4);
+      if (apn) {
+        aprow = (iseg.n - 1) & 15;
+        apoff = (size_t)min(id, nbm1) * blockbytes + (size_t)((iseg.n - 1) & (a.BS - 1)) * rowstride;
+        const size_t roff = ((size_t)iseg.b * a.Hkv + g) * TL::ROWB;
+        if ((lane & 15) == aprow) {
+#pragma unroll
+          for (int i = 0; i < TL::KLD; ++i)
+            knew[i] = *(const u32x4*)((const char*)a.knew + roff + (4 * i + grp) * 16);
+        }
+        if (lane / TL::CPRS == aprow % TL::TPI)
+          vnew = *(const u32x4*)((const char*)a.vnew + roff + (lane % TL::CPRS) * 16);
+      }
+    }
     if (idone) return;
     if (itile + 1 < iseg.thi) {
       ++itile;
@@ -717,6 +748,21 @@ void pa_decode_kernel(DecodeParams a) {
   while (!done) {
 #pragma unroll
     for (int r = 0; r < TL::PF; ++r) {
+      if constexpr (APPEND) {
+        if (apn) {                                      // this tile holds the new token
+          const bool kl = (lane & 15) == aprow;
+          const bool vl = lane / TL::CPRS == aprow % TL::TPI;
+#pragma unroll
+          for (int i = 0; i < TL::KLD; ++i) kr[r][i] = kl ? knew[i] : kr[r][i];
+#pragma unroll
+          for (int j = 0; j < TL::VLD; ++j) vr[r][j] = (vl && j == aprow / TL::TPI) ? vnew : vr[r][j];
+          if (kl) {
+#pragma unroll
+            for (int i = 0; i < TL::KLD; ++i) *(u32x4*)((char*)kbase + apoff + (4 * i + grp) * 16) = knew[i];
+          }
+          if (vl) *(u32x4*)((char*)vbase + apoff + (lane % TL::CPRS) * 16) = vnew;
+        }
+      }
       const f32x4 sc = part1(kr[r], vr[r], qc);
       __builtin_amdgcn_sched_barrier(0);
       issue(kr[r], vr[r]);                              // set r is free again
@@ -1193,16 +1239,12 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
 
 // ------------------------------------------------------------------ KV write scatter
 
-// One workgroup per new token; each thread moves 8 elements (16 source bytes) per step.
+// Row i of key/value (row_elems elements each) into slot s of the caches; the calling
+// workgroup's threads each move 8 elements (16 source bytes) per step.
 template <bool SRC_BF, bool TO_FP8>
-__global__ __launch_bounds__(256) void kv_write_kernel(const void* key, const void* value,
-                                                      void* key_cache, void* value_cache,
-                                                      const int64_t* slots, long long nslots,
-                                                      int row_elems, float k_scale,
-                                                      float v_scale) {
-  const int i = blockIdx.x;
-  const long long s = slots[i];
-  if (s < 0 || s >= nslots) return;
+__device__ __forceinline__ void write_row(const void* key, const void* value, void* key_cache, void* value_cache,
+                                          long long i, long long s, int row_elems, float k_scale,
+                                          float v_scale) {
   const int chunks = row_elems >> 3;
   for (int c = threadIdx.x; c < 2 * chunks; c += 256) {
     const bool isv = c >= chunks;
@@ -1228,6 +1270,34 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* key, const vo
       *(u32x2*)(cache + (size_t)s * row_elems + (size_t)cc * 8) = o;
     }
   }
+}
+
+// One workgroup per new token.
+template <bool SRC_BF, bool TO_FP8>
+__global__ __launch_bounds__(256) void kv_write_kernel(const void* key, const void* value,
+                                                      void* key_cache, void* value_cache,
+                                                      const int64_t* slots, long long nslots,
+                                                      int row_elems, float k_scale,
+                                                      float v_scale) {
+  const int i = blockIdx.x;
+  const long long s = slots[i];
+  if (s < 0 || s >= nslots) return;
+  write_row<SRC_BF, TO_FP8>(key, value, key_cache, value_cache, i, s, row_elems, k_scale, v_scale);
+}
+
+// One workgroup per sequence: its new row goes to position n - 1, the slot read from the
+// block table (ids clamped into the pool); sequences with n = 0 have no new token.
+__global__ __launch_bounds__(256) void kv_append_kernel(const void* key, const void* value, void* key_cache,
+                                                       void* value_cache, const int32_t* bt,
+                                                       const int32_t* lens, int max_blocks, int cap,
+                                                       int bs_shift, int num_blocks, int row_elems) {
+  const int b = blockIdx.x;
+  const int n = clamp_len(lens[b], cap);
+  if (n == 0) return;
+  const int t = n - 1;
+  const unsigned id = min((unsigned)bt[(size_t)b * max_blocks + (t >> bs_shift)], (unsigned)(num_blocks - 1));
+  const long long s = ((long long)id << bs_shift) + (t & ((1 << bs_shift) - 1));
+  write_row<true, false>(key, value, key_cache, value_cache, b, s, row_elems, 1.f, 1.f);
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -1260,6 +1330,20 @@ void launch_decode_policy(const DecodeParams& p, hipStream_t st) {
   else
     hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED, POLICY>), dim3(p.W, HG), dim3(64 * nw), lds, st,
                        p);
+}
+
+// The balanced decode with the step's new rows appended in the same launch (16-bit caches).
+template <int D, int KV, bool BF>
+void launch_decode_append(const DecodeParams& p, bool shared_blocks, hipStream_t st) {
+  const int HG = head_groups(p.Hkv);
+  const int nw = waves_per_group(p.Hkv);
+  const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
+  if (shared_blocks)
+    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED, kCachedPolicy, true>), dim3(p.W, HG),
+                       dim3(64 * nw), lds, st, p);
+  else
+    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED, kStreamPolicy, true>), dim3(p.W, HG),
+                       dim3(64 * nw), lds, st, p);
 }
 
 template <int D, int KV, bool BF>
@@ -1511,6 +1595,8 @@ static DecodeParams make_params(void* out, const void* query, const void* key_ca
   p.v_scale = v_scale;
   p.t0 = 0;
   p.slot0 = 0;
+  p.knew = nullptr;
+  p.vnew = nullptr;
   return p;
 }
 
@@ -1578,6 +1664,53 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                     q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, q_dtype,
                     kv_dtype, k_scale, v_scale, max_context_len, partition_size, tmp_out, max_logits,
                     exp_sums, flags, stream);
+}
+
+int paged_attn_decode_append(void* out, const void* query, const void* key, const void* value,
+                             void* key_cache, void* value_cache, const int32_t* block_tables, int max_blocks,
+                             const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, float scale, int dtype,
+                             int max_context_len, int partition_size, float* tmp_out, float* max_logits,
+                             float* exp_sums, int flags, void* stream) {
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                            num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                            dtype, dtype, 1.f, 1.f, max_context_len, partition_size, tmp_out, max_logits,
+                            exp_sums, flags);
+  if (rc != PKV_OK) return rc > 0 ? PKV_OK : rc;
+  if (!key || !value) return PKV_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_ALIGN;
+  if ((long long)num_kv_heads * head_dim > (1 << 24)) return PKV_ERR_SHAPE;
+  const int Pslots = slots_of(max_context_len, partition_size);
+  if (partition_size != 0 && Pslots == 0) return PKV_OK;   // every context is empty: no new token
+  if (partition_size > 0 && Pslots > 65535) return PKV_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (check_mode()) {
+    const int cr = check_tables(block_tables, max_blocks, context_lens, num_seqs, block_size, num_blocks,
+                                max_context_len, 0, st);
+    if (cr != PKV_OK) return cr;
+  }
+  DecodeParams p = make_params(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                               num_seqs, 1, num_heads, num_kv_heads, block_size, num_blocks, scale, 1.f, 1.f,
+                               max_context_len, partition_size, Pslots, tmp_out, max_logits, exp_sums);
+  const bool sh = (flags & PKV_FLAG_SHARED_BLOCKS) != 0;
+  const bool bf = dtype == PKV_BF16;
+  if (partition_size < 0) {
+    p.knew = key;
+    p.vnew = value;
+    if (head_dim == 128) {
+      if (bf) launch_decode_append<128, KBF16, true>(p, sh, st); else launch_decode_append<128, KF16, false>(p, sh, st);
+    } else {
+      if (bf) launch_decode_append<64, KBF16, true>(p, sh, st); else launch_decode_append<64, KF16, false>(p, sh, st);
+    }
+  } else {
+    // other schedules: the append scatter, then the decode
+    hipLaunchKernelGGL(kv_append_kernel, dim3(num_seqs), dim3(256), 0, st, key, value, key_cache, value_cache,
+                       block_tables, context_lens, max_blocks, p.cap, (int)__builtin_ctz((unsigned)block_size),
+                       num_blocks, num_kv_heads * head_dim);
+    launch_decode_dt(p, head_dim, dtype, dtype, sh, st);
+  }
+  return launch_status();
 }
 
 int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,

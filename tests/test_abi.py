@@ -30,7 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"paged_kv_write", "paged_attn_decode", "paged_attn_reduce", "paged_kv_copy_blocks",
-                          "paged_attn_multi_query", "paged_attn_decode_shared_prefix",
+                          "paged_attn_multi_query", "paged_attn_decode_shared_prefix", "paged_attn_decode_append",
                           "paged_attn_shared_prefix_slots", "paged_attn_prefix_split",
                           "paged_kv_swap_blocks", "pkv_bm_create", "pkv_bm_append", "pkv_bm_check",
                           "paged_attn_workspace_bytes", "paged_attn_partial_slots",
@@ -155,6 +155,32 @@ def test_shared_prefix_slots():
     assert L.paged_attn_shared_prefix_slots(100, 0, 64, 512) == E_SHAPE
     assert L.paged_attn_prefix_split(0, 32, 8, 2048) == 0            # invalid: no device query
     assert L.paged_attn_prefix_split(4, 32, 8, 0) == 0
+
+
+def _ap(**kw):
+    args = dict(out=A, q=A, k=A, v=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, Hq=8, Hkv=2, D=64, BS=16,
+                NB=80, scale=0.125, dt=0, maxlen=256, PS=0, tmp=None, ml=None, es=None, flags=0, stream=None)
+    args.update(kw)
+    return pk.lib().paged_attn_decode_append(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=2), E_DTYPE),                     # fp8 caches keep paged_kv_write + paged_attn_decode
+    (dict(k=None), E_NULL),
+    (dict(v=None), E_NULL),
+    (dict(k=MIS), E_ALIGN),
+    (dict(out=None), E_NULL),
+    (dict(PS=-64), E_WS),
+    (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(D=96), E_SHAPE),
+    (dict(flags=2), E_SHAPE),
+])
+def test_append_rejects(kw, want):
+    assert _ap(**kw) == want
+
+
+def test_append_zero_sequences_is_a_noop():
+    assert _ap(B=0, q=None, out=None, k=None) == OK
 
 
 def test_shared_prefix_zero_sequences_is_a_noop():
