@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per pool copy)")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "swap", "multi_query"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "swap", "multi_query", "graphs"],
                     help="decode: the decode step (default); copy_blocks / swap: the whole-block operations "
                          "on a pool of the workload's block shape")
     ap.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks / swap call")
@@ -296,6 +296,51 @@ def multi_query_op(args):
     print(json.dumps(res), flush=True)
 
 
+def graphs_op(args):
+    """Step time (write -> decode -> reduce) eager and as the replay of the smallest captured HIP
+    graph that fits, for several batch sizes of the workload's shapes (the first B sequences)."""
+    from paged_kv_cache_224_amd.graphs import StepGraphs
+    dev = torch.device("cuda:0")
+    cfg = I.CONFIGS[args.workload]
+    w = I.make_workload(cfg)
+    fp8 = cfg.kv_dtype == "fp8"
+    pools, _ = device_pools(w, dev, 1)
+    kc, vc = pools[0]
+    sizes = [1 << i for i in range(0, 12) if (1 << (i - 1) if i else 0) < cfg.B]
+    g = StepGraphs(kc, vc, cfg.Hq, cfg.max_blocks, cfg.max_len, I.DTYPES[cfg.q_dtype], sizes,
+                   k_scale=w.k_scale, v_scale=w.v_scale)
+    rows = []
+    for B in sorted({1, 4, 16, cfg.B} & set(range(1, cfg.B + 1))):
+        q, kn, vn, sl, bt, ln = g.inputs(B)
+        q.copy_(w.q[:B])
+        kn.copy_(w.k_new[:B])
+        vn.copy_(w.v_new[:B])
+        sl.copy_(torch.from_numpy(w.slot_mapping[:B]))
+        bt.copy_(torch.from_numpy(w.block_tables[:B]))
+        ln.copy_(torch.from_numpy(w.context_lens[:B]))
+        times = {}
+        for mode in ("eager", "graph"):
+            run = (lambda: g._step(B)) if mode == "eager" else (lambda: g.replay(B))
+            for _ in range(args.warmup):
+                run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                run()
+            torch.cuda.synchronize()
+            times[mode] = 1e6 * (time.perf_counter() - t0) / args.steps
+        rows.append({"batch": B, "captured_size": g.size_for(B), "eager_us": round(times["eager"], 2),
+                     "graph_us": round(times["graph"], 2),
+                     "step_time_saved": round(1 - times["graph"] / times["eager"], 4)})
+        print(f"[bench] graphs B={B}: eager {times['eager']:.1f} us, graph {times['graph']:.1f} us",
+              file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "decode step time, eager calls vs replay of the smallest captured HIP graph",
+                      "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": False, "data": "synthetic", "dtype": "fp8" if fp8 else cfg.kv_dtype,
+                      "config": {"workload": cfg.name, "captured_sizes": sizes,
+                                 "partition_size": g.partition_size}, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -309,6 +354,9 @@ def main():
         return
     if args.op == "multi_query":
         multi_query_op(args)
+        return
+    if args.op == "graphs":
+        graphs_op(args)
         return
     if args.op != "decode":
         block_ops(args)
