@@ -82,15 +82,13 @@ def copy_reference(mib):
 
 def measured_traffic(workload, schedule):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of
-    this workload, or None if there is none or the kernel source changed since it was taken."""
-    import hashlib
+    this workload, or None if there is none or the kernel code changed since it was taken."""
+    from paged_kv_cache_224_amd.profile_summary import source_hash
     path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.json")
     if schedule != "balanced" or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "paged_kv_cache_224_amd", "csrc", "pagedkv.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return int(rec["decode_traffic_bytes"]) if rec.get("kernel_source_sha256_16") == h else None
+    return int(rec["decode_traffic_bytes"]) if rec.get("kernel_source_sha256_16") == source_hash() else None
 
 
 def decode_bytes(w):

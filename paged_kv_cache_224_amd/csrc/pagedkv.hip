@@ -7,9 +7,10 @@
 // token and is bound by memory bandwidth (same page, section 7).  How it is computed here is
 // designed for CDNA4:
 //
-//  * Work unit = one wave (64 lanes) per (sequence b, KV head g, token partition p).  The G
-//    query heads that share KV head g are the 16 columns of the MFMA tiles, so every K/V byte
-//    is read from HBM once and used by all G heads.
+//  * Work unit = one wave (64 lanes) per KV head g over a stretch of tiles: a range of the
+//    batch's (sequence, tile) stream (balanced split), one token partition, or one sequence.
+//    The G query heads that share KV head g are the 16 columns of the MFMA tiles, so every
+//    K/V byte is read from HBM once and used by all G heads.
 //  * A tile is 16 consecutive tokens of one KV head, always inside one physical block (block
 //    sizes are multiples of 16).  Scores S^T[16 tok x 16 head] = K[16 x D] . Q^T[D x 16] use
 //    v_mfma_f32_16x16x32_{bf16,f16}; each lane loads its A-operand slice of K straight from
@@ -30,6 +31,12 @@
 //  * The next tile's loads are issued before the current tile is computed.
 //  * Split-K: partials (m, l, o) per partition, merged by paged_attn_reduce with log-sum-exp
 //    weights.  Reduction orders are fixed, so results are deterministic.
+//  * Shared prefix (pa_prefix_kernel): when every row starts with the same blocks, the prefix is
+//    scored against many rows' queries at once -- a dense product on the matrix cores with K/V
+//    stages in LDS -- and merged with each row's suffix partials from the decode above.
+//  * Append (pa_decode_kernel<..., APPEND>): the step's new K/V row is used in place of the
+//    stale pool row and stored into the pool by the wave that streams its tile, so the KV write
+//    needs no launch of its own.
 
 #include <hip/hip_runtime.h>
 

@@ -26,8 +26,18 @@ SRC = os.path.join(ROOT, "paged_kv_cache_224_amd", "csrc", "pagedkv.hip")
 COPY_MIB = 1024
 
 
-def source_hash() -> str:
-    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+def source_hash(path: str = SRC) -> str:
+    """sha256[:16] of the kernel source's code: // comments, trailing blanks and empty lines
+    are dropped first, so editing a comment keeps the recorded measurements."""
+    code = []
+    for line in open(path, encoding="utf-8").read().splitlines():
+        cut = line.find("//")
+        if cut >= 0:
+            line = line[:cut]
+        line = line.rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def commands(workload: str, schedule: str, out: str = "OUT") -> list:
@@ -66,7 +76,7 @@ def summarize(out: str, workload: str, schedule: str = "balanced") -> str:
     h = source_hash()
 
     lines = [f"# {workload}: rocprofv3 summary of the benchmark step ({schedule} schedule)", "",
-             f"Kernel source sha256[:16] = `{h}` (paged_kv_cache_224_amd/csrc/pagedkv.hip)", "",
+             f"Kernel source sha256[:16] = `{h}` (paged_kv_cache_224_amd/csrc/pagedkv.hip without comments)", "",
              "## Commands (run from the repository root on one MI355X; OUT is any scratch folder)", "",
              "```"] + commands(workload, schedule) + [
              f"python -m paged_kv_cache_224_amd.profile_summary OUT {workload} {schedule}", "```", "",
