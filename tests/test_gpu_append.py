@@ -24,12 +24,20 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _small(name, **kw):
-    return I.make_workload(I.shrink(I.CONFIGS[name], **kw))
-
-
 CASES = [("tiny", {}), ("llama3_8b", dict(B=7, len_div=4)), ("long_ctx", dict(B=2, len_div=32)),
-         ("shared_prefix", dict(B=9, len_div=4))]
+         ("shared_prefix", dict(B=9, len_div=4)), ("hkv16_g1", None), ("hkv1_g16_bs64", None)]
+
+
+def _small(name, **kw):
+    if name == "hkv16_g1":          # two KV-head groups per workgroup grid, one query head each
+        cfg = dataclasses.replace(I.CONFIGS["llama3_8b"], name=name, seed=71, B=5, Hq=16, Hkv=16,
+                                  lens=("uniform", 1, 700), max_len=700)
+        return I.make_workload(cfg)
+    if name == "hkv1_g16_bs64":     # one KV head for 16 query heads, 64-token blocks
+        cfg = dataclasses.replace(I.CONFIGS["tiny"], name=name, seed=72, B=6, Hq=16, Hkv=1, block_size=64,
+                                  lens=("uniform", 1, 600), max_len=640, partition_size=128)
+        return I.make_workload(cfg)
+    return I.make_workload(I.shrink(I.CONFIGS[name], **kw))
 
 
 def _nan_new_slots(kc, vc, w):
@@ -79,7 +87,7 @@ def _same_bytes(a, b):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_append_equals_write_then_decode(case):
     name, kw = case
-    w = _small(name, **kw)
+    w = _small(name, **(kw or {}))
     kc_ref, vc_ref = oracle_pools(w)
     ref = oracle_decode(w, kc_ref, vc_ref)
     for PS in _schedules(w):

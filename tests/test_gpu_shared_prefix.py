@@ -72,6 +72,9 @@ CASES = [
     ("fp8_g8_d128_bs32", _prefix_cfg("llama3_70b_fp8", "sp_c", 20, 320, 5, 200, seed=23), (64, 112)),
     ("bf16_g4_d128_bs64", _prefix_cfg("shared_prefix", "sp_d", 33, 192, 16, 300, seed=24, block_size=64), (128,)),
     ("f16_fp8_d64", _prefix_cfg("tiny", "sp_e", 3, 48, 1, 40, seed=25, kv_dtype="fp8"), (16, 48)),
+    ("bf16_g16_hkv1_d64", _prefix_cfg("tiny", "sp_f", 11, 80, 1, 60, seed=26, Hq=16, Hkv=1, q_dtype="bf16",
+                                      kv_dtype="bf16"), (32, 80)),
+    ("bf16_g1_hkv16", _prefix_cfg("shared_prefix", "sp_g", 5, 64, 1, 50, seed=27, Hq=16, Hkv=16), (64, 16)),
 ]
 
 
