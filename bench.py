@@ -64,6 +64,25 @@ def parse():
     return ap.parse_args()
 
 
+def copy_gbps(mib=1024, reps=10):
+    """Read + write GB/s of a plain device-to-device copy of mib MiB (HIP events around the
+    copies): a second yardstick beside the 8 TB/s peak, measured on the same GPU."""
+    n = mib * 2 ** 20 // 4
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    return 2 * mib * 2 ** 20 / dt / 1e9
+
+
 def copy_reference(mib):
     """Plain device-to-device copies of a known size: the HBM counters of this kernel calibrate
     FETCH_SIZE / WRITE_SIZE (each copy reads and writes exactly mib MiB)."""
@@ -522,6 +541,9 @@ def main():
     }
     if w.prefix_blocks.size:
         res["logical_gbps"] = round(step_bytes_logical / (ms_per_step * 1e-3) / 1e9, 1)
+    # second yardstick: a plain 1 GiB device copy measured on the same GPU (after the timed region)
+    cg = copy_gbps()
+    res["copy_reference"] = {"copy_read_plus_write_gbps": round(cg, 1), "decode_frac_of_copy": round(achieved / cg, 4)}
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
