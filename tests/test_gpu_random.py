@@ -1,0 +1,87 @@
+"""Seeded randomized GPU parity: random draws over the supported set, against the fp64 oracle.
+
+Each case draws a head layout (Hkv, group size up to 16), head dim, block size, (query, cache)
+dtype pair, batch size and maximum length; then context lengths that mix uniform draws with the
+values where tiles and blocks turn over (0, 1, 15, 16, 17, block_size - 1, block_size,
+block_size + 1, the maximum); optionally rows that share their first blocks with row 0; and a
+schedule (single pass, fixed partitions, the balanced split at the device's width or at a random
+small width).  Every case also runs multi-query with a random q_len that fits the 16 MFMA
+columns.  The structure varies where the hand-written cases are fixed; the bar is the same.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_224_amd as pk
+from gpu_common import DEV, gpu_decode, gpu_pools, max_err, tolerance
+from paged_kv_cache_224_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+NCASES = 120
+DTYPE_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8"), ("f16", "fp8")]
+
+
+def _draw(seed):
+    rng = np.random.default_rng(1000 + seed)
+    Hkv = int(rng.choice([1, 2, 3, 4, 8, 12, 16]))
+    G = int(rng.choice([g for g in (1, 2, 3, 4, 6, 8, 16) if g * Hkv <= 192]))
+    D = int(rng.choice([64, 128]))
+    BS = int(rng.choice([16, 32, 64, 128, 256]))
+    qdt, kvdt = DTYPE_PAIRS[int(rng.integers(len(DTYPE_PAIRS)))]
+    B = int(rng.integers(1, 25))
+    maxL = int(rng.integers(1, 1501))
+    cfg = I.Config(f"rand{seed}", 2000 + seed, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, block_size=BS, q_dtype=qdt,
+                   kv_dtype=kvdt, lens=("uniform", maxL, maxL), pool=("factor", 1.25), max_len=maxL,
+                   partition_size=BS * int(rng.integers(1, 5)))
+    special = [0, 1, 15, 16, 17, BS - 1, BS, BS + 1, maxL]
+    lens = rng.integers(0, maxL + 1, size=B)
+    for i in range(B):
+        if rng.random() < 0.4:
+            lens[i] = special[int(rng.integers(len(special)))]
+    lens = np.clip(lens, 0, maxL).astype(np.int32)
+    share = int(rng.integers(0, -(-maxL // BS) + 1)) if rng.random() < 0.5 else 0
+    sched = int(rng.integers(4))
+    W = int(rng.integers(1, 300))
+    L = int(rng.choice([l for l in (2, 3, 4, 8) if G * l <= 16] or [1]))
+    return cfg, lens, share, sched, W, L
+
+
+def _oracle_pools(w):
+    if w.cfg.kv_dtype == "fp8":
+        return oracle.quantize_pool(w.k_pool, w.k_scale), oracle.quantize_pool(w.v_pool, w.v_scale)
+    return w.k_pool, w.v_pool
+
+
+@pytest.mark.parametrize("seed", range(NCASES))
+def test_random_case(seed):
+    cfg, lens, share, sched, W, L = _draw(seed)
+    w = I.make_workload(cfg)
+    bt = w.block_tables.copy()
+    if share:
+        bt[1:, :share] = bt[0, :share]             # rows that begin with row 0's first blocks
+    w = dataclasses.replace(w, context_lens=lens, block_tables=bt)
+    kvt = torch.uint8 if cfg.kv_dtype == "fp8" else I.DTYPES[cfg.kv_dtype]
+    PS = [0, cfg.partition_size, pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], kvt), -W][sched]
+    print(f"[random {seed}] Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} BS={cfg.block_size} {cfg.q_dtype}/{cfg.kv_dtype} "
+          f"B={cfg.B} max={cfg.max_len} share={share} PS={PS} L={L} lens={lens.tolist()}", flush=True)
+    kc_ref, vc_ref = _oracle_pools(w)
+    kvdt = "fp8" if cfg.kv_dtype == "fp8" else None
+    ref = oracle.attn(w.q, kc_ref, vc_ref, bt, lens, w.scale, w.k_scale, w.v_scale, kvdt)
+    kc, vc = gpu_pools(w, write_step=False)
+    got = gpu_decode(w, kc, vc, PS, max_context_len=cfg.max_len, shared_blocks=bool(share))
+    assert max_err(got, ref) <= tolerance(cfg)
+    assert np.all(got[lens == 0] == 0)
+    if L > 1:
+        q = I.multi_query_q(cfg, L, seed=seed)
+        mref = oracle.attn_multi_query(q, kc_ref, vc_ref, bt, lens, w.scale, w.k_scale, w.v_scale, kvdt)
+        mPS = PS if PS <= 0 else cfg.partition_size
+        ws = pk.DecodeWorkspace(cfg.B, L * cfg.Hq, cfg.D, cfg.max_len, mPS, device=DEV)
+        out = torch.full((cfg.B, L, cfg.Hq, cfg.D), float("nan"), dtype=I.DTYPES[cfg.q_dtype], device=DEV)
+        pk.multi_query(out, q.to(DEV), kc, vc, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV),
+                       w.scale, ws, w.k_scale, w.v_scale, shared_blocks=bool(share))
+        torch.cuda.synchronize()
+        assert max_err(out.float().cpu().numpy(), mref) <= tolerance(cfg)
