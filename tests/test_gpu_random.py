@@ -85,3 +85,79 @@ def test_random_case(seed):
                        w.scale, ws, w.k_scale, w.v_scale, shared_blocks=bool(share))
         torch.cuda.synchronize()
         assert max_err(out.float().cpu().numpy(), mref) <= tolerance(cfg)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shared_prefix(seed):
+    """paged_attn_decode_shared_prefix on random draws: a prefix of whole blocks that every row
+    names, rows of any length (shorter than the prefix too), a random prefix partition."""
+    cfg, lens, _, _, W, _ = _draw(500 + seed)
+    rng = np.random.default_rng(3000 + seed)
+    nb = -(-cfg.max_len // cfg.block_size)
+    P = cfg.block_size * int(rng.integers(0, nb + 1))
+    P = min(P, (cfg.max_len // cfg.block_size) * cfg.block_size)
+    w = I.make_workload(cfg)
+    bt = w.block_tables.copy()
+    if P:
+        bt[1:, :P // cfg.block_size] = bt[0, :P // cfg.block_size]
+    w = dataclasses.replace(w, context_lens=lens, block_tables=bt)
+    pps = 16 * int(rng.integers(1, 40))
+    PS = -W if rng.random() < 0.5 else None
+    print(f"[random prefix {seed}] Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} BS={cfg.block_size} "
+          f"{cfg.q_dtype}/{cfg.kv_dtype} B={cfg.B} max={cfg.max_len} prefix={P} pps={pps} PS={PS}", flush=True)
+    kc_ref, vc_ref = _oracle_pools(w)
+    kvdt = "fp8" if cfg.kv_dtype == "fp8" else None
+    ref = oracle.attn(w.q, kc_ref, vc_ref, bt, lens, w.scale, w.k_scale, w.v_scale, kvdt)
+    kc, vc = gpu_pools(w, write_step=False)
+    kvt = torch.uint8 if cfg.kv_dtype == "fp8" else I.DTYPES[cfg.kv_dtype]
+    if PS is None:
+        PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], kvt)
+    ws = pk.SharedPrefixWorkspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.max_len, P, PS, pps, device=DEV)
+    out = torch.full((cfg.B, cfg.Hq, cfg.D), float("nan"), dtype=I.DTYPES[cfg.q_dtype], device=DEV)
+    pk.decode_shared_prefix(out, w.q.to(DEV), kc, vc, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV),
+                            w.scale, ws, w.k_scale, w.v_scale)
+    torch.cuda.synchronize()
+    assert max_err(out.float().cpu().numpy(), ref) <= tolerance(cfg)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_append(seed):
+    """paged_attn_decode_append on random draws (16-bit caches, private blocks): equal bit for
+    bit to paged_kv_write at position n - 1 followed by paged_attn_decode, and to the oracle."""
+    cfg, lens, _, sched, W, _ = _draw(700 + seed)
+    if cfg.kv_dtype == "fp8":
+        cfg = dataclasses.replace(cfg, kv_dtype=cfg.q_dtype)
+    w = I.make_workload(cfg)
+    BS = cfg.block_size
+    b = np.arange(cfg.B)
+    pos = np.maximum(lens.astype(np.int64) - 1, 0)
+    slots = np.where(lens > 0, w.block_tables[b, pos // BS].astype(np.int64) * BS + pos % BS, -1)
+    w = dataclasses.replace(w, context_lens=lens, slot_mapping=slots)
+    PS = [0, cfg.partition_size, pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], I.DTYPES[cfg.kv_dtype]),
+          -W][sched]
+    print(f"[random append {seed}] Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} BS={BS} {cfg.q_dtype} B={cfg.B} "
+          f"max={cfg.max_len} PS={PS}", flush=True)
+    kc_ref, vc_ref = w.k_pool.clone(), w.v_pool.clone()
+    oracle.kv_write(w.k_new, w.v_new, kc_ref, vc_ref, slots)
+    ref = oracle.attn(w.q, kc_ref, vc_ref, w.block_tables, lens, w.scale)
+    q, kn, vn = w.q.to(DEV), w.k_new.to(DEV), w.v_new.to(DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    outs, pools = [], []
+    for fused in (True, False):
+        kc, vc = w.k_pool.to(DEV), w.v_pool.to(DEV)
+        ws = pk.DecodeWorkspace(cfg.B, cfg.Hq, cfg.D, cfg.max_len, PS, device=DEV)
+        out = torch.full((cfg.B, cfg.Hq, cfg.D), float("nan"), dtype=I.DTYPES[cfg.q_dtype], device=DEV)
+        if fused:
+            pk.decode_append(out, q, kn, vn, kc, vc, bt, ln, w.scale, ws)
+        else:
+            pk.paged_kv_write(kn, vn, kc, vc, torch.from_numpy(slots).to(DEV))
+            pk.decode(out, q, kc, vc, bt, ln, w.scale, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+        pools.append((kc.cpu(), vc.cpu()))
+    assert torch.equal(outs[0], outs[1])
+    for x, y in zip(pools[0], pools[1]):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    assert torch.equal(pools[0][0].view(torch.uint8), kc_ref.view(torch.uint8))
+    assert max_err(outs[0].float().numpy(), ref) <= tolerance(cfg)
