@@ -12,6 +12,7 @@ kernel's roofline (algorithmic bytes per launch / its mean HIP-event duration) a
 CPU oracle timed on this host's cores.
 """
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -44,6 +45,9 @@ def parse():
                     help="explicit partition_size (overrides --schedule; <0 = balanced over -N workgroups)")
     ap.add_argument("--prefix-partition-size", type=int, default=None,
                     help="shared_prefix schedule: prefix tokens per partition (default: one workgroup per CU)")
+    ap.add_argument("--kv-dtype", default=None, choices=["bf16", "f16", "fp8"],
+                    help="run the workload's shapes with this cache dtype instead of its own (the query "
+                         "dtype stays); the workload is then named <workload>:kv=<dtype>")
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", action="store_true",
@@ -62,6 +66,14 @@ def parse():
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only copy a buffer of this size 5 times (reference for HBM traffic counters)")
     return ap.parse_args()
+
+
+def workload_cfg(args):
+    """The workload's configuration, with the cache dtype of --kv-dtype if given."""
+    cfg = I.CONFIGS[args.workload]
+    if args.kv_dtype and args.kv_dtype != cfg.kv_dtype:
+        cfg = dataclasses.replace(cfg, kv_dtype=args.kv_dtype, name=f"{cfg.name}:kv={args.kv_dtype}")
+    return cfg
 
 
 def copy_gbps(mib=1024, reps=10):
@@ -147,7 +159,7 @@ def cpu_baseline(w, min_seconds):
 def block_ops(args):
     """Whole-block operations on pools of the workload's block shape: copy-on-write copies
     (HBM, read + write) or swap out to / in from pinned host memory (host link)."""
-    cfg = I.CONFIGS[args.workload]
+    cfg = workload_cfg(args)
     dev = torch.device("cuda:0")
     fp8 = cfg.kv_dtype == "fp8"
     dt = torch.uint8 if fp8 else I.DTYPES[cfg.kv_dtype]
@@ -262,7 +274,7 @@ def multi_query_op(args):
     clock.  Algorithmic bytes: the KV rows once (shared by the L tokens), L query rows and L
     output rows per (sequence, head), the used table entries and lengths."""
     dev = torch.device("cuda:0")
-    cfg = I.CONFIGS[args.workload]
+    cfg = workload_cfg(args)
     L = args.q_len
     w = I.make_workload(cfg)
     fp8 = cfg.kv_dtype == "fp8"
@@ -318,7 +330,7 @@ def graphs_op(args):
     graph that fits, for several batch sizes of the workload's shapes (the first B sequences)."""
     from paged_kv_cache_224_amd.graphs import StepGraphs
     dev = torch.device("cuda:0")
-    cfg = I.CONFIGS[args.workload]
+    cfg = workload_cfg(args)
     w = I.make_workload(cfg)
     fp8 = cfg.kv_dtype == "fp8"
     pools, _ = device_pools(w, dev, 1)
@@ -379,7 +391,7 @@ def main():
         block_ops(args)
         return
     dev = torch.device("cuda:0")
-    cfg = I.CONFIGS[args.workload]
+    cfg = workload_cfg(args)
     if args.partition_size is not None:
         PS = args.partition_size
     elif args.schedule in ("balanced", "shared_prefix"):
@@ -392,7 +404,7 @@ def main():
     schedule = "single" if PS == 0 else ("fixed" if PS > 0 else "balanced")
     cascade = args.schedule == "shared_prefix"
     if cascade:
-        schedule = "shared_prefix" 
+        schedule = "shared_prefix"
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     w = I.make_workload(cfg)
     B, Hq, D = cfg.B, cfg.Hq, cfg.D
