@@ -480,6 +480,19 @@ void pa_decode_kernel(DecodeParams a) {
     cur = src.from_lane(0, lane);
     if (!cur.valid) return;
   }
+  // Issue priority by progress (balanced split: every wave of the workgroup streams the same
+  // tiles of its own head).  The sequencer favours a SIMD's older wave, so with equal priority
+  // the first wave on each SIMD runs ahead and the second streams the last ~15% of the tiles
+  // alone at half the loads in flight.  Each wave starts at the highest level and steps down
+  // a level per quarter of its tiles, so a wave that falls behind gets the issue slots.
+  int prog = 0, pq1 = 0, pq2 = 0, pq3 = 0;
+  if constexpr (MODE == MODE_BALANCED) {
+    const int tot = (int)(src.hi - src.lo);
+    pq1 = tot >> 2;
+    pq2 = tot >> 1;
+    pq3 = tot - (tot >> 2);
+    __builtin_amdgcn_s_setprio(3);
+  }
 
   // ---- per-lane constants
   // MFMA column hh = (query head hh / L of the group, new query token hh % L).  Token i of the
@@ -755,6 +768,12 @@ void pa_decode_kernel(DecodeParams a) {
   while (!done) {
 #pragma unroll
     for (int r = 0; r < TL::PF; ++r) {
+      if constexpr (MODE == MODE_BALANCED) {
+        if (prog == pq1) __builtin_amdgcn_s_setprio(2);
+        if (prog == pq2) __builtin_amdgcn_s_setprio(1);
+        if (prog == pq3) __builtin_amdgcn_s_setprio(0);
+        ++prog;
+      }
       if constexpr (APPEND) {
         if (apn) {                                      // this tile holds the new token
           const bool kl = (lane & 15) == aprow;
