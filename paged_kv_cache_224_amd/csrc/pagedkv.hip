@@ -1019,14 +1019,40 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
   // column's limit); otherwise the exponent is one fma per score.
   auto compute = [&](const char* st, int tok0, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    // Every LDS operand of the stage's QK^T, and the V operands of the first PV half, is
+    // requested before the first MFMA; the second half's V reads go out before the softmax.
+    // LDS reads of a wave return in order, so each MFMA waits only for its own operand and
+    // the LDS latency is paid about once per stage instead of once per MFMA.
+    const char* vst = st + PT::KST;
+    auto vread = [&](int sub, int T) {
+      return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)((lds_char*)(vst + sub * PT::SUB) + troff[T])));
+    };
+    u32x4 kf[4][PT::NS];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int s = 0; s < PT::NS; ++s) kf[u][s] = *(const u32x4*)(st + u * PT::SUB + koff[s]);
+    u32x2 vlo[2][PT::NT], vhi[2][PT::NT];
+#pragma unroll
+    for (int T = 0; T < PT::NT; ++T) {
+      vlo[0][T] = vread(0, T);
+      vhi[0][T] = vread(1, T);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 sc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < PT::NS; ++s)
-        sc[u] = mfma_16x16x32<BF>(*(const u32x4*)(st + u * PT::SUB + koff[s]), qv[s], sc[u]);
+      for (int s = 0; s < PT::NS; ++s) sc[u] = mfma_16x16x32<BF>(kf[u][s], qv[s], sc[u]);
     }
+#pragma unroll
+    for (int T = 0; T < PT::NT; ++T) {
+      vlo[1][T] = vread(2, T);
+      vhi[1][T] = vread(3, T);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float x[4][4];
     float mx;
     if constexpr (MASKED) {
@@ -1085,17 +1111,14 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
         }
       }
     }
-    const char* vst = st + PT::KST;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const u32x4 pb = {pop[2 * h].x, pop[2 * h].y, pop[2 * h + 1].x, pop[2 * h + 1].y};
       accL = mfma_16x16x32<BF>(ones, pb, accL);
 #pragma unroll
       for (int T = 0; T < PT::NT; ++T) {
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)((lds_char*)(vst + (2 * h) * PT::SUB) + troff[T])));
-        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)((lds_char*)(vst + (2 * h + 1) * PT::SUB) + troff[T])));
+        const u32x2 lo = vlo[h][T];
+        const u32x2 hi = vhi[h][T];
         u32x4 va;
         if constexpr (MASKED)
           va = u32x4{lo.x & vm[2 * h].x, lo.y & vm[2 * h].y, hi.x & vm[2 * h + 1].x, hi.y & vm[2 * h + 1].y};
