@@ -140,6 +140,61 @@ def summarize(out: str, workload: str, schedule: str = "balanced") -> str:
     return text
 
 
+# Core counters of one pass (at most 8 SQ and 2 GRBM counters fit in one rocprofv3 pass).
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+               "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def sq_commands(workload: str, schedule: str, out: str = "OUT") -> list:
+    """The one counter pass that sq_summary() reads."""
+    return [f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {out}/sq -o run -- python -u bench.py "
+            f"--workload {workload} --schedule {schedule} --no-cpu-baseline --steps 5 --warmup 2"]
+
+
+def sq_summary(out: str, workload: str, schedule: str = "balanced") -> str:
+    """profiles/counters_<schedule>_<workload>.md: per kernel of the step, instructions per wave, the
+    MFMA pipe's busy share per SIMD, the share of wave cycles spent waiting, LDS bank conflicts."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    meta = {}
+    for r in csv.DictReader(open(os.path.join(out, "sq", "run_counter_collection.csv"))):
+        k = r["Kernel_Name"]
+        if not any(t in k for t in ("pa_decode", "pa_prefix", "pa_reduce", "kv_write")):
+            continue
+        vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        meta[k] = int(r["Grid_Size"])
+    lines = [f"# {workload}: core counters of the benchmark step ({schedule} schedule)", "",
+             f"Kernel source sha256[:16] = `{source_hash()}` (paged_kv_cache_224_amd/csrc/pagedkv.hip without "
+             "comments)", "", "## Commands (run from the repository root on one MI355X; OUT is any scratch folder)",
+             "", "```"] + sq_commands(workload, schedule) + [
+             f"python -c \"from paged_kv_cache_224_amd.profile_summary import sq_summary; "
+             f"sq_summary('OUT', '{workload}', '{schedule}')\"", "```", "",
+             "Means over the dispatches of the run.  Counters are summed over the whole GPU.  Definitions:",
+             "- per wave: an instruction count / (grid threads / 64);",
+             "- MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), the share of the CUs' busy "
+             "cycles in which a SIMD's matrix pipe works;",
+             "- waiting: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share of wave cycles spent waiting for an operand "
+             "or a counter;",
+             "- LDS bank conflicts: SQ_LDS_BANK_CONFLICT, cycles stalled on conflicts (whole GPU).", "",
+             "| kernel | waves | MFMA / wave | VALU / wave | LDS / wave | MFMA busy per SIMD | waiting | "
+             "LDS bank-conflict cycles |", "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(vals):
+        m = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        waves = max(1, meta[k] // 64)
+        busy = m.get("SQ_BUSY_CU_CYCLES", 0.0)
+        mfma_busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * busy) if busy else 0.0
+        wc = m.get("SQ_WAVE_CYCLES", 0.0)
+        wait = m.get("SQ_WAIT_INST_ANY", 0.0) / wc if wc else 0.0
+        lines.append(f"| {k[:80]} | {waves} | {m.get('SQ_INSTS_MFMA', 0) / waves:.0f} | "
+                     f"{m.get('SQ_INSTS_VALU', 0) / waves:.0f} | {m.get('SQ_INSTS_LDS', 0) / waves:.0f} | "
+                     f"{100 * mfma_busy:.1f}% | {100 * wait:.1f}% | {m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+    lines.append("")
+    text = "\n".join(lines)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"counters_{schedule}_{workload}.md"), "w") as fh:
+        fh.write(text)
+    return text
+
+
 if __name__ == "__main__":
     if len(sys.argv) < 3:
         sys.exit(__doc__)
