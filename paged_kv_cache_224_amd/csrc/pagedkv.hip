@@ -482,16 +482,29 @@ void pa_decode_kernel(DecodeParams a) {
   }
   // Issue priority by progress (balanced split: every wave of the workgroup streams the same
   // tiles of its own head).  The sequencer favours a SIMD's older wave, so with equal priority
-  // the first wave on each SIMD runs ahead and the second streams the last ~15% of the tiles
-  // alone at half the loads in flight.  Each wave starts at the highest level and steps down
-  // a level per quarter of its tiles, so a wave that falls behind gets the issue slots.
+  // the first wave on each SIMD (waves 0-3 of a full workgroup) runs ahead and the second
+  // (waves 4-7, on the same SIMDs) finishes ~6% of the launch later.
+  //  - 16-bit caches, 8-wave workgroups: each wave publishes its tile count in LDS and compares
+  //    it with its SIMD partner's (wave wl ^ 4) every tile; the wave that is ahead drops to the
+  //    lowest priority, the one behind takes the highest.  The pair stays within a tile.
+  //  - otherwise (fp8 caches, whose widening keeps the SIMD busy and gains from one wave running
+  //    ahead; workgroups of fewer waves): each wave starts at the highest level and steps down
+  //    a level per quarter of its tiles.
+  // Priorities only order instruction issue; no result depends on them.
   int prog = 0, pq1 = 0, pq2 = 0, pq3 = 0;
+  __shared__ int progs[kMaxWaves];                      // tiles started, per wave
+  const bool pairs = MODE == MODE_BALANCED && KV != KFP8 && (blockDim.x >> 6) == kMaxWaves;
   if constexpr (MODE == MODE_BALANCED) {
     const int tot = (int)(src.hi - src.lo);
     pq1 = tot >> 2;
     pq2 = tot >> 1;
     pq3 = tot - (tot >> 2);
-    __builtin_amdgcn_s_setprio(3);
+    if (pairs) {
+      __hip_atomic_store(&progs[wl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __builtin_amdgcn_s_setprio(1);
+    } else {
+      __builtin_amdgcn_s_setprio(3);
+    }
   }
 
   // ---- per-lane constants
@@ -769,9 +782,21 @@ void pa_decode_kernel(DecodeParams a) {
 #pragma unroll
     for (int r = 0; r < TL::PF; ++r) {
       if constexpr (MODE == MODE_BALANCED) {
-        if (prog == pq1) __builtin_amdgcn_s_setprio(2);
-        if (prog == pq2) __builtin_amdgcn_s_setprio(1);
-        if (prog == pq3) __builtin_amdgcn_s_setprio(0);
+        if (pairs) {
+          __hip_atomic_store(&progs[wl], prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          const int d = prog - __builtin_amdgcn_readfirstlane(
+                                   __hip_atomic_load(&progs[wl ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+          if (d > 0)
+            __builtin_amdgcn_s_setprio(0);
+          else if (d < 0)
+            __builtin_amdgcn_s_setprio(3);
+          else
+            __builtin_amdgcn_s_setprio(1);
+        } else {
+          if (prog == pq1) __builtin_amdgcn_s_setprio(2);
+          if (prog == pq2) __builtin_amdgcn_s_setprio(1);
+          if (prog == pq3) __builtin_amdgcn_s_setprio(0);
+        }
         ++prog;
       }
       if constexpr (APPEND) {
