@@ -602,8 +602,10 @@ void pa_decode_kernel(DecodeParams a) {
   reset();
 
   // First half of a tile: scores S^T = K . Q^T and the V tile into LDS.  After it the tile's
-  // registers are free, so the next tile's loads can land in them.
-  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4* qv) -> f32x4 {
+  // registers are free, so the next tile's loads can land in them.  In the tile that holds the
+  // sequence's end, V rows >= n go to LDS as zeros (stale bytes may be NaN, and a zero
+  // probability times NaN would still be NaN); every other tile stores its rows unchanged.
+  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4* qv, int tile, int n) -> f32x4 {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < TL::NS; ++st) {
@@ -628,19 +630,39 @@ void pa_decode_kernel(DecodeParams a) {
         *(u32x4*)(vtile + vslot[r]) = vr[r];
       }
     }
+    const int valid = n - (tile << 4);                  // rows of this tile below n
+    if (valid < 16) {
+      // Overwrite the rows >= n.  The empty asm keeps the compiler from folding these stores
+      // into selects on the stores above, which would cost every tile the masking.
+      asm volatile("" ::: "memory");
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < TL::VLD; ++r) {
+        if (r * TL::TPI + lane / TL::CPRS >= valid) {
+          *(u32x4*)(vtile + vslot[r]) = zero;
+          if constexpr (KV == KFP8) *(u32x4*)(vtile + vslot2[r]) = zero;
+        }
+      }
+    }
     return s;
   };
 
   // Second half: online softmax (exp2 domain) and O^T += V^T . P^T.  Tokens a column may not
-  // see (>= n, or newer than its own query token) are selected out of the scores, and V rows
-  // >= n are zeroed (stale bytes may be NaN).  A column that has seen no token yet keeps
-  // m = -inf; its probabilities are computed against 0 so that they come out 0, not NaN.
+  // see (>= n, or newer than its own query token) are selected out of the scores; a tile that
+  // every column sees whole (all but the last tile or two of a segment) skips the selects.  A
+  // column that has seen no token yet keeps m = -inf; its probabilities are computed against
+  // 0 so that they come out 0, not NaN.
   auto part2 = [&](int tile, int n, f32x4 s) {
     const int tbase = (tile << 4) + 4 * grp;
-    const int lim = n - hidden;
     float x[4];
+    if (((tile + 1) << 4) <= n - (a.L - 1)) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (tbase + e < lim) ? s[e] * a.c2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) x[e] = s[e] * a.c2;
+    } else {
+      const int lim = n - hidden;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (tbase + e < lim) ? s[e] * a.c2 : -INFINITY;
+    }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_rows32(max_rows16(mx));
     if (__ballot(mx > m) != 0) {
@@ -661,18 +683,10 @@ void pa_decode_kernel(DecodeParams a) {
       lsum += from16<BF>(ph[e]);
     }
     const u32x2 pop = {pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
-    unsigned vm0 = 0xffffffffu, vm1 = 0xffffffffu;
-    if (n - (tile << 4) < 16) {
-      vm0 = ((tbase + 0 < n) ? 0x0000ffffu : 0u) | ((tbase + 1 < n) ? 0xffff0000u : 0u);
-      vm1 = ((tbase + 2 < n) ? 0x0000ffffu : 0u) | ((tbase + 3 < n) ? 0xffff0000u : 0u);
-    }
 #pragma unroll
     for (int T = 0; T < TL::NT; ++T) {
       s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)vtile + troff[T]));
-      u32x2 vt = __builtin_bit_cast(u32x2, raw);
-      vt.x &= vm0;
-      vt.y &= vm1;
-      acc[T] = mfma_16x16x16<BF>(vt, pop, acc[T]);
+      acc[T] = mfma_16x16x16<BF>(__builtin_bit_cast(u32x2, raw), pop, acc[T]);
     }
   };
 
@@ -814,7 +828,7 @@ void pa_decode_kernel(DecodeParams a) {
           if (vl) *(u32x4*)((char*)vbase + apoff + (lane % TL::CPRS) * 16) = vnew;
         }
       }
-      const f32x4 sc = part1(kr[r], vr[r], qc);
+      const f32x4 sc = part1(kr[r], vr[r], qc, tile, cur.n);
       __builtin_amdgcn_sched_barrier(0);
       issue(kr[r], vr[r]);                              // set r is free again
       __builtin_amdgcn_sched_barrier(0);
