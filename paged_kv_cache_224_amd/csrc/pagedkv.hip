@@ -488,12 +488,13 @@ void pa_decode_kernel(DecodeParams a) {
   //    it with its SIMD partner's (wave wl ^ 4) every tile; the wave that is ahead drops to the
   //    lowest priority, the one behind takes the highest.  The pair stays within a tile.
   //  - otherwise (fp8 caches, whose widening keeps the SIMD busy and gains from one wave running
-  //    ahead; workgroups of fewer waves): each wave starts at the highest level and steps down
-  //    a level per quarter of its tiles.
+  //    ahead; workgroups of fewer waves; a last head group whose partner wave has no head):
+  //    each wave starts at the highest level and steps down a level per quarter of its tiles.
   // Priorities only order instruction issue; no result depends on them.
   int prog = 0, pq1 = 0, pq2 = 0, pq3 = 0;
   __shared__ int progs[kMaxWaves];                      // tiles started, per wave
-  const bool pairs = MODE == MODE_BALANCED && KV != KFP8 && (blockDim.x >> 6) == kMaxWaves;
+  const bool pairs = MODE == MODE_BALANCED && KV != KFP8 && (blockDim.x >> 6) == kMaxWaves &&
+                     blockIdx.y * kMaxWaves + (wl ^ 4) < a.Hkv;   // the partner has a head
   if constexpr (MODE == MODE_BALANCED) {
     const int tot = (int)(src.hi - src.lo);
     pq1 = tot >> 2;
