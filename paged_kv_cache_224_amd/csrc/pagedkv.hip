@@ -290,11 +290,20 @@ __device__ __forceinline__ int tiles_after(int n, int t0) {
   const int t = ((n + 15) >> 4) - t0;
   return t > 0 ? t : 0;
 }
+// Units the balanced split counts for such a sequence: one per tile, plus one in front of its
+// first tile.  Every sequence a workgroup starts costs it a segment switch and a split-K partial
+// (about one tile of streaming time, measured), so the extra unit keeps workgroups that start
+// many short sequences from finishing last.
+__device__ __forceinline__ int units_after(int n, int t0) {
+  const int t = tiles_after(n, t0);
+  return t > 0 ? t + 1 : 0;
+}
 
-// Balanced split of the batch's (sequence, tile) stream of N tiles into Weff contiguous
-// ranges whose sizes differ by at most one: the first `rem` ranges hold q+1 tiles, the rest
-// q.  Weff is the requested count, lowered so that q >= kMinChunkTiles.  32-bit arithmetic
-// (N < 2^31 is checked on the host).
+// Balanced split of the batch's unit stream (units_after: each sequence is one unit followed
+// by one unit per tile) of N units into Weff contiguous ranges whose sizes differ by at most
+// one: the first `rem` ranges hold q+1 units, the rest q.  A workgroup processes the tiles
+// whose units fall in its range.  Weff is the requested count, lowered so that
+// q >= kMinChunkTiles.  32-bit arithmetic (N < 2^31 is checked on the host).
 struct Split {
   int N, Weff, q, rem;
   Split() = default;
@@ -338,13 +347,14 @@ struct SegSource {
   __device__ __forceinline__ int len(int b) const {
     return clamp_len(__builtin_amdgcn_readfirstlane(lens[b]), cap);
   }
-  // Table of sequences b .. b+63 given b's first tile; n_lane = len(b + lane) if already known.
+  // Table of sequences b .. b+63 given b's first unit; n_lane = len(b + lane) if already known.
+  // st_v is the unit of the lane's first tile (past its sequence's leading unit).
   __device__ __forceinline__ void fill(int b, long long start, int lane, int n_lane) {
     b0 = b;
     base = start;
     n_v = n_lane;
     const int t = tiles_after(n_v, t0);
-    st_v = wave_incl_scan(t) - t;
+    st_v = wave_incl_scan(units_after(n_v, t0)) - t;
     const long long s0 = start + st_v;
     vmask = __ballot(t > 0 && s0 < hi && s0 + t > lo);
   }
@@ -456,7 +466,7 @@ void pa_decode_kernel(DecodeParams a) {
       const int bb = lane * per + i;
       const int n = bb < B ? clamp_len(a.lens[bb], cap) : 0;
       if (i == 0) n_first = n;
-      run += tiles_after(n, src.t0);
+      run += units_after(n, src.t0);
     }
     const int incl = wave_incl_scan(run);               // inclusive scan over lanes
     const int N = __builtin_amdgcn_readlane(incl, 63);
@@ -1248,12 +1258,12 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
   if (PS > 0) {
     P = (n + PS - 1) / PS;
   } else {
-    int total = 0, before = 0;               // tiles of the whole batch, of sequences < b
+    int total = 0, before = 0;               // split units of the whole batch, of sequences < b
     for (int i0 = 0; i0 < B; i0 += 64) {
       const int i = i0 + lane;
-      const int t = i < B ? tiles_after(clamp_len(lens[i], cap), t0) : 0;
-      total += t;
-      before += i < b ? t : 0;
+      const int u = i < B ? units_after(clamp_len(lens[i], cap), t0) : 0;
+      total += u;
+      before += i < b ? u : 0;
     }
     total = __builtin_amdgcn_readlane(wave_incl_scan(total), 63);
     before = __builtin_amdgcn_readlane(wave_incl_scan(before), 63);
@@ -1262,7 +1272,8 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
       P = 0;
     } else {
       const Split split(total, -PS);
-      P = split.owner(before + nt - 1) - split.owner(before) + 1;
+      const int first = before + 1;          // the unit of b's first tile
+      P = split.owner(first + nt - 1) - split.owner(first) + 1;
     }
   }
   P = min(slot0 + P, Pslots);
@@ -1620,7 +1631,7 @@ static int check_attn(void* out, const void* query, const void* key_cache, const
       (tmp_out && !aligned(tmp_out, 16)) || (max_logits && !aligned(max_logits, 4)) ||
       (exp_sums && !aligned(exp_sums, 4)))
     return PKV_ERR_ALIGN;
-  if ((long long)num_seqs * ((max_context_len + 15) / 16) >= (1LL << 31)) return PKV_ERR_SHAPE;
+  if ((long long)num_seqs * ((max_context_len + 15) / 16 + 1) >= (1LL << 31)) return PKV_ERR_SHAPE;
   return PKV_OK;
 }
 
