@@ -1403,8 +1403,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const void* key, const v
 // ------------------------------------------------------------------ host helpers
 
 // Partial slots per (sequence, head): fixed partitions need ceil(max_len / PS); a balanced
-// split gives every workgroup >= kMinChunkTiles tiles, so a sequence meets at most
-// ceil(tiles / kMinChunkTiles) + 1 ranges.
+// split gives every workgroup >= kMinChunkTiles units, and a sequence's tiles are consecutive
+// units, so a sequence meets at most ceil(tiles / kMinChunkTiles) + 1 ranges.
 int slots_of(int max_context_len, int partition_size) {
   if (partition_size > 0) return (max_context_len + partition_size - 1) / partition_size;
   if (partition_size < 0) {
