@@ -585,14 +585,16 @@ void pa_decode_kernel(DecodeParams a) {
     return a.bt[(size_t)b * a.max_blocks + (tile >> tshift)];
   };
   // Raw buffer loads: the descriptor base is the tile's first row (scalar), the lane offsets
-  // are fixed VGPRs, and the descriptor's range covers exactly the tile's rows of head g.
-  // Block ids outside [0, num_blocks) are clamped so no access leaves the pool.
-  auto load_tile = [&](unsigned id, int tile, u32x4* kd, u32x4* vd) {
+  // are fixed VGPRs, and the descriptor's range covers exactly the tile's rows of head g
+  // (span bytes; a span of 0 puts every lane out of range: the loads return zeros without
+  // touching memory).  Block ids outside [0, num_blocks) are clamped so no access leaves the
+  // pool.
+  auto load_tile = [&](unsigned id, int tile, u32x4* kd, u32x4* vd, int span) {
     const size_t off = (size_t)min(id, nbm1) * blockbytes + (size_t)(tile & tmask) * 16 * rowstride;
     const __amdgpu_buffer_rsrc_t kres =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, tile_span, kBufWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, span, kBufWord3);
     const __amdgpu_buffer_rsrc_t vres =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, tile_span, kBufWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, span, kBufWord3);
 #pragma unroll
     for (int i = 0; i < TL::KLD; ++i)
       kd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 0, POLICY));
@@ -752,9 +754,10 @@ void pa_decode_kernel(DecodeParams a) {
   int itile = cur.tlo;
   bool idone = false;
   int nid = load_id(cur.b, cur.tlo);
-  // Load the tile at the issue position, then advance it and fetch the next block id (past
-  // the stream's end the last tile is loaded again: an L2 hit that keeps every load
-  // unconditional).
+  // Load the tile at the issue position, then advance it and fetch the next block id.  Past
+  // the stream's end the same load instructions go out with an empty range (zeros, no memory
+  // traffic), which keeps every load unconditional: a skipped load would make the compiler
+  // wait for every load in flight before the next tile.
   // Append state of the tile in flight: whether it holds the new token, the token's row in the
   // tile, the pool offset of that row (head g), and the new row's values for the lanes that
   // hold it in the A operand (K) and in the V load pattern.
@@ -764,7 +767,7 @@ void pa_decode_kernel(DecodeParams a) {
   u32x4 knew[APPEND ? TL::KLD : 1], vnew;
   auto issue = [&](u32x4* kd, u32x4* vd) {
     const unsigned id = (unsigned)__builtin_amdgcn_readfirstlane(nid);
-    load_tile(id, itile, kd, vd);
+    load_tile(id, itile, kd, vd, idone ? 0 : tile_span);
     if constexpr (APPEND) {
       apn = !idone && itile == ((iseg.n - 1) >> 4);
       if (apn) {
