@@ -128,9 +128,10 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
  *                      tmp_out   [b][h][p] = v_scale * sum_t exp(s_t - m_p) V_t / l_p
  *                    Must be a multiple of 16 and of block_size.
  *                    < 0: split-K over a balanced schedule: the batch's 16-token tiles, in
- *                    (sequence, position) order, are cut into W = -partition_size equal
- *                    contiguous ranges (fewer if a range would drop below 8 tiles), one per
- *                    workgroup, so every workgroup moves the same number of bytes whatever
+ *                    (sequence, position) order, each sequence's tiles preceded by one extra
+ *                    unit for the cost of starting it, are cut into W = -partition_size equal
+ *                    contiguous ranges of units (fewer if a range would drop below 8 units),
+ *                    one per workgroup, so every workgroup does about the same work whatever
  *                    the length mix.  Each (sequence, range) overlap writes one partial
  *                    (m, l, o as above, over the tokens of that overlap) at slot
  *                    p = range - (range of the sequence's first tile).
