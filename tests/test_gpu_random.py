@@ -9,6 +9,7 @@ small width).  Every case also runs multi-query with a random q_len that fits th
 columns.  The structure varies where the hand-written cases are fixed; the bar is the same.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -21,7 +22,20 @@ from paged_kv_cache_224_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-NCASES = 120
+
+def _seeds(var, lo, hi):
+    """Seed range of a randomized test: [lo, hi) by default, or "A:B" from the environment
+    variable (a longer sweep with the same checks, e.g. PKV_RANDOM_SEEDS=1000:1600)."""
+    spec = os.environ.get(var)
+    if spec:
+        a, b = spec.split(":")
+        return range(int(a), int(b))
+    return range(lo, hi)
+
+
+DECODE_SEEDS = _seeds("PKV_RANDOM_SEEDS", 0, 120)
+PREFIX_SEEDS = _seeds("PKV_RANDOM_PREFIX_SEEDS", 0, 30)
+APPEND_SEEDS = _seeds("PKV_RANDOM_APPEND_SEEDS", 0, 30)
 DTYPE_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8"), ("f16", "fp8")]
 
 
@@ -56,7 +70,7 @@ def _oracle_pools(w):
     return w.k_pool, w.v_pool
 
 
-@pytest.mark.parametrize("seed", range(NCASES))
+@pytest.mark.parametrize("seed", DECODE_SEEDS)
 def test_random_case(seed):
     cfg, lens, share, sched, W, L = _draw(seed)
     w = I.make_workload(cfg)
@@ -87,7 +101,7 @@ def test_random_case(seed):
         assert max_err(out.float().cpu().numpy(), mref) <= tolerance(cfg)
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", PREFIX_SEEDS)
 def test_random_shared_prefix(seed):
     """paged_attn_decode_shared_prefix on random draws: a prefix of whole blocks that every row
     names, rows of any length (shorter than the prefix too), a random prefix partition."""
@@ -120,7 +134,7 @@ def test_random_shared_prefix(seed):
     assert max_err(out.float().cpu().numpy(), ref) <= tolerance(cfg)
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", APPEND_SEEDS)
 def test_random_append(seed):
     """paged_attn_decode_append on random draws (16-bit caches, private blocks): equal bit for
     bit to paged_kv_write at position n - 1 followed by paged_attn_decode, and to the oracle."""
