@@ -19,7 +19,8 @@
 //  * Online softmax in the exp2 domain on the MFMA output layout: lane l holds 4 tokens of
 //    head l%16, so the tile max needs two cross-lane steps and the running sum stays
 //    lane-local until the end.  Tokens past the context are removed by select, never by
-//    multiplying, and their V rows are zeroed, so stale NaN bytes cannot leak in.
+//    multiplying, and their K/V rows are read as zeros (the last tile's loads end at the
+//    sequence's last row), so stale NaN bytes cannot leak in.
 //  * O^T[D x 16 head] += V^T[D x 16 tok] . P^T[16 tok x 16 head] with v_mfma_f32_16x16x16.
 //    V is staged through LDS in an XOR-swizzled layout and read back with gfx950's
 //    ds_read_b64_tr_b16, which hands each lane 4 tokens of one d: exactly the operand layout.
@@ -615,10 +616,10 @@ void pa_decode_kernel(DecodeParams a) {
   reset();
 
   // First half of a tile: scores S^T = K . Q^T and the V tile into LDS.  After it the tile's
-  // registers are free, so the next tile's loads can land in them.  In the tile that holds the
-  // sequence's end, V rows >= n go to LDS as zeros (stale bytes may be NaN, and a zero
-  // probability times NaN would still be NaN); every other tile stores its rows unchanged.
-  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4* qv, int tile, int n) -> f32x4 {
+  // registers are free, so the next tile's loads can land in them.  Rows >= n of a sequence's
+  // last tile arrive as zeros (their loads are out of the tile's buffer range), so stale bytes,
+  // which may be NaN, never reach the scores or the V tile.
+  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4* qv) -> f32x4 {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < TL::NS; ++st) {
@@ -641,20 +642,6 @@ void pa_decode_kernel(DecodeParams a) {
         *(u32x4*)(vtile + vslot2[r]) = hi;
       } else {
         *(u32x4*)(vtile + vslot[r]) = vr[r];
-      }
-    }
-    const int valid = n - (tile << 4);                  // rows of this tile below n
-    if (valid < 16) {
-      // Overwrite the rows >= n.  The empty asm keeps the compiler from folding these stores
-      // into selects on the stores above, which would cost every tile the masking.
-      asm volatile("" ::: "memory");
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int r = 0; r < TL::VLD; ++r) {
-        if (r * TL::TPI + lane / TL::CPRS >= valid) {
-          *(u32x4*)(vtile + vslot[r]) = zero;
-          if constexpr (KV == KFP8) *(u32x4*)(vtile + vslot2[r]) = zero;
-        }
       }
     }
     return s;
@@ -754,7 +741,8 @@ void pa_decode_kernel(DecodeParams a) {
   int itile = cur.tlo;
   bool idone = false;
   int nid = load_id(cur.b, cur.tlo);
-  // Load the tile at the issue position, then advance it and fetch the next block id.  Past
+  // Load the tile at the issue position, then advance it and fetch the next block id.  The
+  // range ends at the sequence's last row, so rows >= n of its last tile read as zeros.  Past
   // the stream's end the same load instructions go out with an empty range (zeros, no memory
   // traffic), which keeps every load unconditional: a skipped load would make the compiler
   // wait for every load in flight before the next tile.
@@ -767,7 +755,8 @@ void pa_decode_kernel(DecodeParams a) {
   u32x4 knew[APPEND ? TL::KLD : 1], vnew;
   auto issue = [&](u32x4* kd, u32x4* vd) {
     const unsigned id = (unsigned)__builtin_amdgcn_readfirstlane(nid);
-    load_tile(id, itile, kd, vd, idone ? 0 : tile_span);
+    const int rows = iseg.n - (itile << 4);             // rows of the tile below n (>= 1)
+    load_tile(id, itile, kd, vd, idone ? 0 : (rows >= 16 ? tile_span : (rows - 1) * rowstride + TL::ROWB));
     if constexpr (APPEND) {
       apn = !idone && itile == ((iseg.n - 1) >> 4);
       if (apn) {
@@ -842,7 +831,7 @@ void pa_decode_kernel(DecodeParams a) {
           if (vl) *(u32x4*)((char*)vbase + apoff + (lane % TL::CPRS) * 16) = vnew;
         }
       }
-      const f32x4 sc = part1(kr[r], vr[r], qc, tile, cur.n);
+      const f32x4 sc = part1(kr[r], vr[r], qc);
       __builtin_amdgcn_sched_barrier(0);
       issue(kr[r], vr[r]);                              // set r is free again
       __builtin_amdgcn_sched_barrier(0);
