@@ -8,8 +8,9 @@ otherwise hold part of a 0.6 GB cache between steps), the step rotates over seve
 the KV pools, so each step reads pools the previous steps did not touch.
 
 Prints one JSON line: whole-step KV GB/s as `value`, plus decode tokens/s, the decode
-kernel's roofline (algorithmic bytes per launch / its mean HIP-event duration) and the fp64
-CPU oracle timed on this host's cores.
+kernel's roofline (algorithmic bytes per launch / its mean duration, from HIP events bound to
+the kernel's own dispatch on every timed step) and the fp64 CPU oracle timed on this host's
+cores (all of them, and one thread).
 """
 import argparse
 import dataclasses
@@ -53,8 +54,11 @@ def parse():
     ap.add_argument("--append", action="store_true",
                     help="16-bit caches, balanced schedule: run the step's KV write inside the decode launch "
                          "(paged_attn_decode_append) instead of paged_kv_write + paged_attn_decode")
-    ap.add_argument("--event-every", type=int, default=5,
-                    help="bracket the decode launch with HIP events on every N-th timed step (1 = all)")
+    ap.add_argument("--event-every", type=int, default=1,
+                    help="time the decode launch with HIP events on every N-th timed step (default: all)")
+    ap.add_argument("--event-mode", default="kernel", choices=["kernel", "marker"],
+                    help="kernel: events bound to the call's kernels (pkv_time_next_call, no packet between "
+                         "kernels); marker: events recorded on the stream before and after the call")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per pool copy)")
@@ -123,19 +127,20 @@ def measured_traffic(workload, schedule):
 
 
 def decode_bytes(w):
-    """Algorithmic bytes of one decode launch: KV rows of every (sequence, token) once, q,
-    the used block-table entries and the context lengths (logical and unique-block counts)."""
+    """Algorithmic bytes of one decode call: KV rows of every (sequence, token) once, the query
+    and output rows, the used block-table entries and the context lengths (logical and
+    unique-block counts).  The output row is counted although in the split-K schedules the
+    merge launch, not the decode launch, writes it; the difference is 0.09% on the Llama-3-8B
+    layer."""
     nb = I.algorithmic_bytes(w)
-    cfg = w.cfg
-    e_q = 2
-    base = cfg.B * cfg.Hq * cfg.D * e_q + 4 * int(w.blocks_used.sum()) + 4 * cfg.B
-    return nb["kv_logical"] + base, nb["kv_unique"] + base, nb
+    return nb["decode_logical"], nb["decode_unique"], nb
 
 
-def cpu_baseline(w, min_seconds):
-    """fp64 oracle (KV write + attention over the whole batch) on this host's cores."""
+def cpu_baseline(w, min_seconds, threads=None, max_reps=50):
+    """fp64 oracle (KV write + attention over the whole batch) on this host's cores (all of
+    them unless `threads` is given)."""
     import oracle
-    threads = len(os.sched_getaffinity(0))
+    threads = threads or len(os.sched_getaffinity(0))
     kvdt = "fp8" if w.cfg.kv_dtype == "fp8" else None
     if kvdt:
         kc = oracle.quantize_pool(w.k_pool, w.k_scale)
@@ -150,7 +155,7 @@ def cpu_baseline(w, min_seconds):
                     nthreads=threads)
         t_total += time.perf_counter() - t0
         reps += 1
-        if reps >= 50:
+        if reps >= max_reps:
             break
     t = t_total / reps
     return t, threads, reps
@@ -432,29 +437,34 @@ def main():
         shared = False
     torch.cuda.synchronize()
 
+    marker = args.event_mode == "marker"
+
+    def timed(call, ev):
+        """Run the attention call; with ev, time it (kernel-bound events, or markers around it)."""
+        if ev is not None:
+            if marker:
+                ev[0].record()
+            else:
+                pk.time_next_call(ev[0], ev[1])
+        call()
+        if ev is not None and marker:
+            ev[1].record()
+
     def step(i, ev=None):
         kc, vc = pools[i % copies]
         if append:                                      # write + decode in one launch, then the merge
-            if ev is not None:
-                ev[0].record()
-            pk.paged_attn_decode_append(None, q, k_new, v_new, kc, vc, bt, lens, w.scale, maxlen, PS, ws.tmp_out,
-                                        ws.max_logits, ws.exp_sums, shared_blocks=shared)
-            if ev is not None:
-                ev[1].record()
+            timed(lambda: pk.paged_attn_decode_append(None, q, k_new, v_new, kc, vc, bt, lens, w.scale, maxlen, PS,
+                                                      ws.tmp_out, ws.max_logits, ws.exp_sums, shared_blocks=shared),
+                  ev)
             pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS)
             return
         pk.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
-        if ev is not None:
-            ev[0].record()
         if cascade:                                     # three kernels: prefix, suffix, merge
-            pk.decode_shared_prefix(out, q, kc, vc, bt, lens, w.scale, sws, w.k_scale, w.v_scale)
-            if ev is not None:
-                ev[1].record()
+            timed(lambda: pk.decode_shared_prefix(out, q, kc, vc, bt, lens, w.scale, sws, w.k_scale, w.v_scale), ev)
             return
-        pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS, ws.tmp_out,
-                             ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale, shared_blocks=shared)
-        if ev is not None:
-            ev[1].record()
+        timed(lambda: pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS,
+                                           ws.tmp_out, ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale,
+                                           shared_blocks=shared), ev)
         if PS != 0:
             pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS)
 
@@ -464,12 +474,17 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps, synchronised on both sides
-    # HIP events bracket the decode launch on every event_every-th timed step (each marker between
-    # two kernels lengthens the step by ~2.5 us, so instrumenting every step would understate
-    # the step rate); the kernel's mean duration comes from those sampled launches
+    # HIP events time the decode call on every event_every-th timed step.  By default they are
+    # bound to the call's kernels (recorded at the first kernel's start and the last kernel's
+    # end), so no marker packet sits between two kernels of the step and the step rate is not
+    # disturbed; --event-mode marker records them on the stream around the call instead.
     every = max(1, args.event_every)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if i % every == 0 else None
            for i in range(args.steps)]
+    for e in evs:                                       # create the HIP events before the timed region
+        if e is not None:
+            e[0].record()
+            e[1].record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -504,6 +519,7 @@ def main():
     step_bytes_logical = nb["decode_logical"] + nb["write"]
     value = step_bytes_unique / (ms_per_step * 1e-3) / 1e9
     dec_mean_ms = float(np.mean(decode_ms))
+    dec_median_ms = float(np.median(decode_ms))
     if append:                                          # the timed launch also moves the new rows
         dec_unique += nb["write"]
     achieved = dec_unique / (dec_mean_ms * 1e-3) / 1e9
@@ -535,7 +551,9 @@ def main():
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "decode_kernel_ms_mean": round(dec_mean_ms, 5),
+        "decode_kernel_ms_median": round(dec_median_ms, 5),
         "decode_event_samples": len(decode_ms),
+        "decode_event_mode": "bound to the kernels (hipExtLaunchKernel)" if not marker else "markers around the call",
         "decode_kernel_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(decode_ms, [10, 50, 90])],
         "step_bytes": {"logical": step_bytes_logical, "unique": step_bytes_unique},
         "roofline": {
@@ -544,6 +562,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac_at_median": round(dec_unique / (dec_median_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "samples": len(decode_ms),
             "traffic": measured_traffic(cfg.name, schedule),
             "kernel": ("pa_prefix_kernel + pa_decode_kernel + pa_reduce_kernel (one call, timed together)"
                        if cascade else ("pa_decode_kernel with the step's KV write appended" if append
@@ -569,6 +589,14 @@ def main():
                       f"({t_cpu:.3f} s each)",
             "tokens_per_s": round(B / t_cpu, 2),
         }
+        # the same oracle on one thread: this workload (one pass) and the tiny workload
+        one = {}
+        for wl in (w, I.make_workload(I.CONFIGS["tiny"])):
+            t1, _, r1 = cpu_baseline(wl, 0.0 if wl is w else 1.0, threads=1, max_reps=1 if wl is w else 50)
+            ab = I.algorithmic_bytes(wl)
+            one[wl.cfg.name] = {"seconds": round(t1, 4), "runs": r1, "tokens_per_s": round(wl.cfg.B / t1, 2),
+                                "gbps": round((ab["decode_unique"] + ab["write"]) / t1 / 1e9, 4)}
+        res["cpu_baseline"]["one_thread"] = {"cores": 1, **one}
     print(json.dumps(res), flush=True)
 
 

@@ -19,7 +19,9 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
- *     nothing, keeps no pointer after returning and never synchronises the device.
+ *     nothing, keeps no pointer after returning and never synchronises the device (the one
+ *     exception, the measurement hook pkv_time_next_call, holds two event handles until the
+ *     next attention call returns).
  *   - All launches go to `stream` (a hipStream_t; NULL = the null stream) and are
  *     asynchronous.  A decode step is paged_kv_write -> paged_attn_decode ->
  *     (paged_attn_reduce), ordered by the stream.
@@ -32,7 +34,9 @@
  *   - Device-resident values (block ids, context lengths, slots) are not read on the host.
  *     Kernels clamp them so that every access stays inside the buffers the sizes describe:
  *     a block id outside [0, num_blocks) or a length beyond the table gives an unspecified
- *     result, never an out-of-bounds access.  With the environment variable PKV_CHECK=1 the
+ *     result for that sequence, never an out-of-bounds access (lengths are clamped to
+ *     max_context_len by every kernel of a call alike, and table indices to the row, so the
+ *     other sequences' results are unaffected).  With the environment variable PKV_CHECK=1 the
  *     library instead copies them to the host (synchronising `stream`), validates them and
  *     returns PKV_ERR_CHECK on a violation.
  */
@@ -380,6 +384,20 @@ int paged_attn_shared_prefix_slots(int max_context_len, int prefix_len, int pref
    workgroup per compute unit of the current HIP device (a multiple of 64).
    Returns 0 if no device is available or an argument is invalid.  Queries the device. */
 int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int prefix_len);
+
+/*
+ * pkv_time_next_call -- measurement hook.  Binds two caller-owned HIP events (hipEvent_t,
+ * created with timing enabled) to the kernels of the NEXT attention call made on the calling
+ * thread (paged_attn_decode, paged_attn_multi_query, paged_attn_decode_append,
+ * paged_attn_decode_shared_prefix or paged_attn_reduce): `start_event` is recorded when that
+ * call's first kernel starts and `stop_event` when its last kernel ends (hipExtLaunchKernel),
+ * so hipEventElapsedTime(start, stop) is the call's GPU execution time with no marker packet
+ * between kernels.  One-shot: the next attention call consumes the events whether or not it
+ * launches anything (a call that fails its checks records nothing).  Either event may be NULL.
+ * Thread-local state; the library keeps the handles only until that call returns.  Returns
+ * PKV_OK.
+ */
+int pkv_time_next_call(void* start_event, void* stop_event);
 
 /* Static English text for a pkv_status value. */
 const char* pkv_status_string(int status);

@@ -7,9 +7,9 @@ is the thin ctypes binding over it plus a seeded synthetic workload generator.
 from ._lib import (BlockManager, DecodeWorkspace, PagedKVError, SharedPrefixWorkspace, balanced_split, decode,
                    decode_append, decode_shared_prefix, lib, multi_query, paged_attn_decode, paged_attn_decode_append, paged_attn_decode_shared_prefix,
                    paged_attn_multi_query, paged_attn_reduce, paged_attn_workspace_bytes, paged_kv_copy_blocks,
-                   paged_kv_swap_blocks, paged_kv_write, prefix_split, status_string)
+                   paged_kv_swap_blocks, paged_kv_write, prefix_split, status_string, time_next_call)
 
 __all__ = ["BlockManager", "DecodeWorkspace", "PagedKVError", "SharedPrefixWorkspace", "balanced_split", "decode",
            "decode_append", "decode_shared_prefix", "lib", "multi_query", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_decode_shared_prefix",
            "paged_attn_multi_query", "paged_attn_reduce", "paged_attn_workspace_bytes", "paged_kv_copy_blocks",
-           "paged_kv_swap_blocks", "paged_kv_write", "prefix_split", "status_string"]
+           "paged_kv_swap_blocks", "paged_kv_write", "prefix_split", "status_string", "time_next_call"]

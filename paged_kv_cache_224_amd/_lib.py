@@ -7,6 +7,7 @@ library has not been built, every call raises ``PagedKVError``; there is no fall
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional
 
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_partial_slots.restype = I
         L.paged_attn_balanced_split.argtypes = [I, I, I, I]
         L.paged_attn_balanced_split.restype = I
+        L.pkv_time_next_call.argtypes = [P, P]
+        L.pkv_time_next_call.restype = I
         L.pkv_status_string.argtypes = [I]
         L.pkv_status_string.restype = ctypes.c_char_p
         L.paged_kv_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
@@ -98,6 +101,13 @@ def status_string(status: int) -> str:
     return lib().pkv_status_string(int(status)).decode()
 
 
+def time_next_call(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
+    """Bind two recorded timing events to the next attention call's kernels on this thread
+    (pkv_time_next_call): afterwards start.elapsed_time(stop) is that call's GPU time.  The
+    events must have been recorded once, so that their HIP events exist."""
+    lib().pkv_time_next_call(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+
+
 def _check(fn: str, status: int) -> None:
     if status != 0:
         raise PagedKVError(fn, status, status_string(status))
@@ -109,6 +119,76 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return t.data_ptr()
+
+
+# ---- argument validation (before any call into the library).  The C ABI receives raw pointers
+# and trusts the sizes it is given; these checks make sure the tensors really have the shapes
+# the kernels index with.  Shapes and dtypes are checked first and the device last, so that
+# every check can run on a machine without a GPU.
+
+_KV16 = (torch.float16, torch.bfloat16)
+_KV8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _shape(name: str, t: torch.Tensor, shape, dtype=None) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _pools(query_dtype, key_cache: torch.Tensor, value_cache: torch.Tensor):
+    """(NB, BS, Hkv, D) of a K/V pool pair of the cache dtype a query dtype allows."""
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache must both be [num_blocks, block_size, num_kv_heads, head_dim] "
+                         "of one dtype")
+    if query_dtype not in _KV16:
+        raise ValueError(f"query dtype must be float16 or bfloat16, not {query_dtype}")
+    if key_cache.dtype != query_dtype and key_cache.dtype not in _KV8:
+        raise ValueError(f"a {key_cache.dtype} cache cannot be read with {query_dtype} queries")
+    return tuple(key_cache.shape)
+
+
+def _tables(block_tables: torch.Tensor, context_lens: torch.Tensor, B: int) -> None:
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}, max_blocks], got {tuple(block_tables.shape)}")
+    if context_lens.dim() != 1 or context_lens.shape[0] != B:
+        raise ValueError(f"context_lens must be [{B}], got {tuple(context_lens.shape)}")
+
+
+def _workspace(tmp_out, max_logits, exp_sums, B: int, rows: int, P: int, D: int) -> None:
+    """Split-K partials: tmp_out fp32 [B', rows, P, D], max_logits / exp_sums fp32 [B', rows, P]
+    with B' >= B (the kernels index sequences b < B only, so a workspace sized for a larger
+    batch serves a smaller one); rows may be given as two dims (q_len, num_heads)."""
+    P = max(P, 1)
+    for name, t, tail in (("tmp_out", tmp_out, (P, D)), ("max_logits", max_logits, (P,)),
+                          ("exp_sums", exp_sums, (P,))):
+        if t is None:
+            raise ValueError(f"{name} is required for split-K")
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+        want = (B, rows) + tail
+        lead = tuple(t.shape[:t.dim() - len(tail)])
+        if tuple(t.shape[t.dim() - len(tail):]) != tail or len(lead) < 2 or lead[0] < B or \
+                math.prod(lead[1:]) != rows:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+
+
+def _on_gpu(**tensors) -> None:
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
 
 
 def _stream(stream) -> Optional[int]:
@@ -125,22 +205,30 @@ def paged_kv_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     """Scatter key/value [T, Hkv, D] into caches [NB, BS, Hkv, D] at slot_mapping [T] (int64).
 
     A uint8 / float8_e4m3fn cache is written as E4M3FN codes of x / scale."""
+    if key.dim() != 3 or key.dtype not in _KV16:
+        raise ValueError("key must be float16/bfloat16 [num_tokens, num_kv_heads, head_dim]")
     T, Hkv, D = key.shape
-    NB, BS, Hkv2, D2 = key_cache.shape
-    if (Hkv2, D2) != (Hkv, D) or value.shape != key.shape or value_cache.shape != key_cache.shape:
-        raise ValueError("shape mismatch")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
-        raise ValueError("slot_mapping must be int64 [T]")
+    NB, BS, Hkv2, D2 = _pools(key.dtype, key_cache, value_cache)
+    if (Hkv2, D2) != (Hkv, D):
+        raise ValueError("key rows and cache rows differ in num_kv_heads or head_dim")
+    _shape("value", value, key.shape, key.dtype)
+    _shape("slot_mapping", slot_mapping, (T,), torch.int64)
+    _on_gpu(key=key, value=value, key_cache=key_cache, value_cache=value_cache, slot_mapping=slot_mapping)
     rc = lib().paged_kv_write(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                               _ptr(slot_mapping), T, NB, BS, Hkv, D, _DT[key.dtype], _DT[key_cache.dtype],
                               float(k_scale), float(v_scale), _stream(stream))
     _check("paged_kv_write", rc)
 
 
+def partial_slots(max_context_len: int, partition_size: int) -> int:
+    """Partial slots per (sequence, row) of a split-K schedule (paged_attn_partial_slots)."""
+    return int(lib().paged_attn_partial_slots(int(max_context_len), int(partition_size)))
+
+
 def workspace_shapes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
                      partition_size: int):
     """(tmp_out, max_logits/exp_sums) shapes for a split-K schedule (partition_size != 0)."""
-    P = max(1, int(lib().paged_attn_partial_slots(int(max_context_len), int(partition_size))))
+    P = max(1, partial_slots(max_context_len, partition_size))
     return (num_seqs, num_heads, P, head_dim), (num_seqs, num_heads, P)
 
 
@@ -160,12 +248,19 @@ def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cach
                       stream=None, shared_blocks: bool = False) -> None:
     """Decode attention; see include/pagedkv.h.  partition_size != 0 writes split-K partials.
     shared_blocks: some physical blocks appear in several table rows (keeps them cached)."""
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_heads, head_dim]")
     B, Hq, D = query.shape
-    NB, BS, Hkv, D2 = key_cache.shape
-    if D2 != D or value_cache.shape != key_cache.shape:
-        raise ValueError("shape mismatch")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
+    NB, BS, Hkv, D2 = _pools(query.dtype, key_cache, value_cache)
+    if D2 != D:
+        raise ValueError("query and cache head_dim differ")
+    _tables(block_tables, context_lens, B)
+    if out is not None:
+        _shape("out", out, query.shape, query.dtype)
+    if partition_size != 0:
+        _workspace(tmp_out, max_logits, exp_sums, B, Hq, partial_slots(max_context_len, partition_size), D)
+    _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
+            context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums)
     rc = lib().paged_attn_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv,
                                  D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
@@ -181,13 +276,21 @@ def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key
                            tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
                            exp_sums: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
                            stream=None, shared_blocks: bool = False) -> None:
-    """query [B, L, Hq, D]: L new tokens per sequence, causal among themselves (include/pagedkv.h)."""
+    """query [B, L, Hq, D]: L new tokens per sequence, causal among themselves (include/pagedkv.h).
+    Split-K partials have L * Hq rows per sequence: tmp_out [B, L * Hq, P, D]."""
+    if query.dim() != 4:
+        raise ValueError("query must be [num_seqs, q_len, num_heads, head_dim]")
     B, Lq, Hq, D = query.shape
-    NB, BS, Hkv, D2 = key_cache.shape
-    if D2 != D or value_cache.shape != key_cache.shape:
-        raise ValueError("shape mismatch")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
+    NB, BS, Hkv, D2 = _pools(query.dtype, key_cache, value_cache)
+    if D2 != D:
+        raise ValueError("query and cache head_dim differ")
+    _tables(block_tables, context_lens, B)
+    if out is not None:
+        _shape("out", out, query.shape, query.dtype)
+    if partition_size != 0:
+        _workspace(tmp_out, max_logits, exp_sums, B, Lq * Hq, partial_slots(max_context_len, partition_size), D)
+    _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
+            context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums)
     rc = lib().paged_attn_multi_query(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                       _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Lq, Hq,
                                       Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
@@ -221,12 +324,22 @@ def paged_attn_decode_append(out: Optional[torch.Tensor], query: torch.Tensor, k
                              shared_blocks: bool = False) -> None:
     """Store key/value [B, Hkv, D] at position n - 1 of every sequence and decode, in one call
     (16-bit caches; include/pagedkv.h).  partition_size != 0 writes split-K partials."""
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_heads, head_dim]")
     B, Hq, D = query.shape
-    NB, BS, Hkv, D2 = key_cache.shape
-    if D2 != D or value_cache.shape != key_cache.shape or key.shape != (B, Hkv, D) or value.shape != key.shape:
-        raise ValueError("shape mismatch")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
+    NB, BS, Hkv, D2 = _pools(query.dtype, key_cache, value_cache)
+    if D2 != D or key_cache.dtype != query.dtype:
+        raise ValueError("paged_attn_decode_append needs 16-bit caches of the query dtype and head_dim")
+    _shape("key", key, (B, Hkv, D), query.dtype)
+    _shape("value", value, (B, Hkv, D), query.dtype)
+    _tables(block_tables, context_lens, B)
+    if out is not None:
+        _shape("out", out, query.shape, query.dtype)
+    if partition_size != 0:
+        _workspace(tmp_out, max_logits, exp_sums, B, Hq, partial_slots(max_context_len, partition_size), D)
+    _on_gpu(out=out, query=query, key=key, value=value, key_cache=key_cache, value_cache=value_cache,
+            block_tables=block_tables, context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits,
+            exp_sums=exp_sums)
     rc = lib().paged_attn_decode_append(
         _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype],
@@ -256,12 +369,20 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_
                                     shared_blocks: bool = False) -> None:
     """Decode of a batch whose rows share their first prefix_len tokens' blocks: prefix pass,
     suffix pass and merge in one call; writes out [B, Hq, D] (include/pagedkv.h)."""
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_heads, head_dim]")
     B, Hq, D = query.shape
-    NB, BS, Hkv, D2 = key_cache.shape
-    if D2 != D or value_cache.shape != key_cache.shape:
-        raise ValueError("shape mismatch")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
+    NB, BS, Hkv, D2 = _pools(query.dtype, key_cache, value_cache)
+    if D2 != D:
+        raise ValueError("query and cache head_dim differ")
+    _tables(block_tables, context_lens, B)
+    _shape("out", out, query.shape, query.dtype)
+    P = int(lib().paged_attn_shared_prefix_slots(int(max_context_len), int(prefix_len), int(prefix_partition_size),
+                                                 int(partition_size)))
+    if P >= 0:                                          # invalid arguments: the library reports them
+        _workspace(tmp_out, max_logits, exp_sums, B, Hq, P, D)
+    _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
+            context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums)
     rc = lib().paged_attn_decode_shared_prefix(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
@@ -314,7 +435,13 @@ def paged_attn_reduce(out: torch.Tensor, tmp_out: torch.Tensor, max_logits: torc
                       exp_sums: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
                       partition_size: int, stream=None) -> None:
     """Log-sum-exp merge of split-K partials into out [B, Hq, D]."""
+    if out.dim() != 3 or out.dtype not in _KV16:
+        raise ValueError("out must be float16/bfloat16 [num_seqs, num_heads, head_dim]")
     B, Hq, D = out.shape
+    if context_lens.dtype != torch.int32 or context_lens.dim() != 1 or context_lens.shape[0] != B:
+        raise ValueError(f"context_lens must be int32 [{B}]")
+    _workspace(tmp_out, max_logits, exp_sums, B, Hq, partial_slots(max_context_len, partition_size), D)
+    _on_gpu(out=out, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums, context_lens=context_lens)
     rc = lib().paged_attn_reduce(_ptr(out), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
                                  _ptr(context_lens), B, Hq, D, int(max_context_len), int(partition_size),
                                  _DT[out.dtype], _stream(stream))
@@ -357,11 +484,14 @@ def decode(out: torch.Tensor, query, key_cache, value_cache, block_tables, conte
 def paged_kv_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, src_blocks: torch.Tensor,
                          dst_blocks: torch.Tensor, stream=None) -> None:
     """Copy whole blocks inside both pools (copy-on-write); src/dst are int32 device tensors."""
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache must be [num_blocks, block_size, num_kv_heads, head_dim]")
     NB, BS, Hkv, D = key_cache.shape
-    if value_cache.shape != key_cache.shape or src_blocks.shape != dst_blocks.shape:
-        raise ValueError("shape mismatch")
+    if src_blocks.dim() != 1 or src_blocks.shape != dst_blocks.shape:
+        raise ValueError("src_blocks and dst_blocks must be 1-D of one length")
     if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32:
         raise ValueError("block ids must be int32")
+    _on_gpu(key_cache=key_cache, value_cache=value_cache, src_blocks=src_blocks, dst_blocks=dst_blocks)
     rc = lib().paged_kv_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(src_blocks), _ptr(dst_blocks),
                                     src_blocks.numel(), NB, BS, Hkv, D, _DT[key_cache.dtype], _stream(stream))
     _check("paged_kv_copy_blocks", rc)
@@ -374,12 +504,21 @@ def paged_kv_swap_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, hos
 
     host_key / host_value must be pinned CPU tensors (pin_memory=True); ids are int32 device
     tensors."""
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache must be [num_blocks, block_size, num_kv_heads, head_dim]")
     NB, BS, Hkv, D = key_cache.shape
     NH = host_key.shape[0]
     if host_key.shape[1:] != key_cache.shape[1:] or host_value.shape != host_key.shape:
         raise ValueError("host pools must have the device pools' block shape")
-    if host_key.dtype != key_cache.dtype or not (host_key.is_pinned() and host_value.is_pinned()):
-        raise ValueError("host pools must be pinned and of the cache dtype")
+    if dev_blocks.dim() != 1 or dev_blocks.shape != host_blocks.shape or dev_blocks.dtype != torch.int32 or \
+            host_blocks.dtype != torch.int32:
+        raise ValueError("dev_blocks and host_blocks must be int32, 1-D of one length")
+    if host_key.dtype != key_cache.dtype or host_value.dtype != key_cache.dtype or host_key.is_cuda or \
+            host_value.is_cuda:
+        raise ValueError("host pools must be CPU tensors of the cache dtype")
+    _on_gpu(key_cache=key_cache, value_cache=value_cache, dev_blocks=dev_blocks, host_blocks=host_blocks)
+    if not (host_key.is_pinned() and host_value.is_pinned()):
+        raise ValueError("host pools must be pinned (pin_memory=True)")
     rc = lib().paged_kv_swap_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(host_key), _ptr(host_value),
                                     _ptr(dev_blocks), _ptr(host_blocks), dev_blocks.numel(), NB, NH, BS, Hkv, D,
                                     _DT[key_cache.dtype], 1 if to_host else 0, _stream(stream))

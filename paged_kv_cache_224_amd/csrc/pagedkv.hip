@@ -40,12 +40,14 @@
 //    needs no launch of its own.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "pagedkv.h"
@@ -248,7 +250,7 @@ struct DecodeParams {
   int PS;          // fixed partitions: tokens per partition
   int Pslots;      // partial slots per (sequence, head) in the workspace
   int W;           // balanced: workgroups per head group
-  int cap;         // context lengths are clamped to [0, cap]
+  int cap;         // context lengths are clamped to [0, cap] (cap = max_context_len, as in the reduce)
   int t0;          // balanced split: tiles skipped at the start of every sequence (a shared
                    // prefix handled elsewhere); the stream holds tiles [t0, ceil(n / 16))
   int slot0;       // partial slots below slot0 belong to someone else (the prefix pass)
@@ -580,10 +582,13 @@ void pa_decode_kernel(DecodeParams a) {
       qv[s] = *(const u32x4*)(qrow + d0 * 2);
     }
   };
-  // Physical block of logical tile `tile` of sequence b (a wave-uniform address; the tile
-  // index is below ceil(n / 16) with n <= max_blocks * BS, so the entry is inside the row).
+  // Physical block of logical tile `tile` of sequence b (a wave-uniform address).  A valid
+  // length keeps the entry index below ceil(n / BS) <= max_blocks; a length past the table only
+  // re-reads the row's last entry, so it spoils that sequence's result alone and never leaves
+  // the table.
+  const int lastcol = a.max_blocks - 1;
   auto load_id = [&](int b, int tile) -> int {
-    return a.bt[(size_t)b * a.max_blocks + (tile >> tshift)];
+    return a.bt[(size_t)b * a.max_blocks + min(tile >> tshift, lastcol)];
   };
   // Raw buffer loads: the descriptor base is the tile's first row (scalar), the lane offsets
   // are fixed VGPRs, and the descriptor's range covers exactly the tile's rows of head g
@@ -1387,12 +1392,46 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const void* key, const v
   const int n = clamp_len(lens[b], cap);
   if (n == 0) return;
   const int t = n - 1;
-  const unsigned id = min((unsigned)bt[(size_t)b * max_blocks + (t >> bs_shift)], (unsigned)(num_blocks - 1));
+  const int col = min(t >> bs_shift, max_blocks - 1);   // a length past the table: its last entry
+  const unsigned id = min((unsigned)bt[(size_t)b * max_blocks + col], (unsigned)(num_blocks - 1));
   const long long s = ((long long)id << bs_shift) + (t & ((1 << bs_shift) - 1));
   write_row<true, false>(key, value, key_cache, value_cache, b, s, row_elems, 1.f, 1.f);
 }
 
 // ------------------------------------------------------------------ host helpers
+
+// Measurement hook (pkv_time_next_call): the caller's events, bound to the kernels of the next
+// attention call on this thread -- the start event to the call's first kernel, the stop event to
+// its last -- so that the elapsed time between them is the kernels' own execution time.
+struct CallTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local CallTimer t_armed;   // set by pkv_time_next_call, taken by the next attention call
+thread_local CallTimer t_call;    // the running call's events
+thread_local bool t_first = true; // the running call has not launched a kernel yet
+
+// Scope of one attention call: takes the armed events (a call that fails its checks drops them).
+struct TimedCall {
+  TimedCall() {
+    t_call = std::exchange(t_armed, CallTimer{});
+    t_first = true;
+  }
+  ~TimedCall() { t_call = CallTimer{}; }
+};
+
+// Every kernel of an attention call is launched here.  `last` marks the call's final kernel.
+// With events bound, hipExtLaunchKernel records them at the kernel's start and end; otherwise a
+// plain launch.
+template <typename F, typename... Args>
+void launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, bool last, Args... args) {
+  const hipEvent_t e0 = t_first ? t_call.start : nullptr;
+  const hipEvent_t e1 = last ? t_call.stop : nullptr;
+  t_first = false;
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, st, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
 
 // Partial slots per (sequence, head): fixed partitions need ceil(max_len / PS); a balanced
 // split gives every workgroup >= kMinChunkTiles units, and a sequence's tiles are consecutive
@@ -1410,18 +1449,17 @@ int waves_per_group(int Hkv) { return Hkv < kMaxWaves ? Hkv : kMaxWaves; }
 int head_groups(int Hkv) { return (Hkv + kMaxWaves - 1) / kMaxWaves; }
 
 template <int D, int KV, bool BF, int POLICY>
-void launch_decode_policy(const DecodeParams& p, hipStream_t st) {
+void launch_decode_policy(const DecodeParams& p, bool last, hipStream_t st) {
   const int HG = head_groups(p.Hkv);
   const int nw = waves_per_group(p.Hkv);
   const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
   if (p.mode == MODE_SINGLE)
-    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_SINGLE, POLICY>), dim3(p.B, HG), dim3(64 * nw), lds, st, p);
+    launch(pa_decode_kernel<D, KV, BF, MODE_SINGLE, POLICY>, dim3(p.B, HG), dim3(64 * nw), lds, st, last, p);
   else if (p.mode == MODE_FIXED)
-    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_FIXED, POLICY>), dim3(p.Pslots, HG, p.B), dim3(64 * nw),
-                       lds, st, p);
+    launch(pa_decode_kernel<D, KV, BF, MODE_FIXED, POLICY>, dim3(p.Pslots, HG, p.B), dim3(64 * nw), lds, st, last,
+           p);
   else
-    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED, POLICY>), dim3(p.W, HG), dim3(64 * nw), lds, st,
-                       p);
+    launch(pa_decode_kernel<D, KV, BF, MODE_BALANCED, POLICY>, dim3(p.W, HG), dim3(64 * nw), lds, st, last, p);
 }
 
 // The balanced decode with the step's new rows appended in the same launch (16-bit caches).
@@ -1431,19 +1469,19 @@ void launch_decode_append(const DecodeParams& p, bool shared_blocks, hipStream_t
   const int nw = waves_per_group(p.Hkv);
   const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
   if (shared_blocks)
-    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED, kCachedPolicy, true>), dim3(p.W, HG),
-                       dim3(64 * nw), lds, st, p);
+    launch(pa_decode_kernel<D, KV, BF, MODE_BALANCED, kCachedPolicy, true>, dim3(p.W, HG), dim3(64 * nw), lds, st,
+           true, p);
   else
-    hipLaunchKernelGGL((pa_decode_kernel<D, KV, BF, MODE_BALANCED, kStreamPolicy, true>), dim3(p.W, HG),
-                       dim3(64 * nw), lds, st, p);
+    launch(pa_decode_kernel<D, KV, BF, MODE_BALANCED, kStreamPolicy, true>, dim3(p.W, HG), dim3(64 * nw), lds, st,
+           true, p);
 }
 
 template <int D, int KV, bool BF>
-void launch_decode(const DecodeParams& p, bool shared_blocks, hipStream_t st) {
+void launch_decode(const DecodeParams& p, bool shared_blocks, bool last, hipStream_t st) {
   if (shared_blocks)
-    launch_decode_policy<D, KV, BF, kCachedPolicy>(p, st);
+    launch_decode_policy<D, KV, BF, kCachedPolicy>(p, last, st);
   else
-    launch_decode_policy<D, KV, BF, kStreamPolicy>(p, st);
+    launch_decode_policy<D, KV, BF, kStreamPolicy>(p, last, st);
 }
 
 template <int D, int KV, bool BF>
@@ -1451,7 +1489,7 @@ void launch_prefix(const PrefixParams& p, hipStream_t st) {
   const long long qblocks = ((long long)p.B * p.G + kPrefixCols - 1) / kPrefixCols;
   const dim3 grid((unsigned)(qblocks * p.hp8));
   const size_t lds = (size_t)PrefixTile<D, KV>::LDS_BYTES;
-  hipLaunchKernelGGL((pa_prefix_kernel<D, KV, BF>), grid, dim3(64 * kPrefixWaves), lds, st, p);
+  launch(pa_prefix_kernel<D, KV, BF>, grid, dim3(64 * kPrefixWaves), lds, st, false, p);
 }
 
 void launch_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
@@ -1459,13 +1497,10 @@ void launch_reduce(void* out, const float* tmp_out, const float* max_logits, con
                    int t0, int slot0, bool bf, hipStream_t st) {
   const dim3 grid((unsigned)(((long long)B * rows_per_seq + 3) / 4)), block(256);
   const int Pm = Pslots > 0 ? Pslots : 1;
-  if (D == 128) {
-    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
-    else    hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
-  } else {
-    if (bf) hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
-    else    hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, block, 0, st, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0, slot0);
-  }
+  auto k = D == 128 ? (bf ? pa_reduce_kernel<128, true> : pa_reduce_kernel<128, false>)
+                    : (bf ? pa_reduce_kernel<64, true> : pa_reduce_kernel<64, false>);
+  launch(k, grid, block, 0, st, true, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0,
+         slot0);
 }
 
 // Partial slots of a shared-prefix decode: the prefix partitions first, then the balanced
@@ -1511,6 +1546,12 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_HOST: return "host buffer is not pinned, mapped host memory of the required size";
     default: return "unknown status";
   }
+}
+
+int pkv_time_next_call(void* start_event, void* stop_event) {
+  t_armed.start = (hipEvent_t)start_event;
+  t_armed.stop = (hipEvent_t)stop_event;
+  return PKV_OK;
 }
 
 int paged_attn_partial_slots(int max_context_len, int partition_size) {
@@ -1664,7 +1705,9 @@ static DecodeParams make_params(void* out, const void* query, const void* key_ca
   p.L = q_len;
   p.mode = partition_size == 0 ? MODE_SINGLE : (partition_size > 0 ? MODE_FIXED : MODE_BALANCED);
   p.W = partition_size < 0 ? -partition_size : 0;
-  p.cap = (int)std::min<long long>(max_context_len, (long long)max_blocks * block_size);
+  // Lengths are clamped to max_context_len, the bound paged_attn_reduce also uses, so both
+  // count the same split units; table indices are clamped to the row separately.
+  p.cap = max_context_len;
   p.Pslots = Pslots;
   p.out = out;
   p.q = query;
@@ -1692,16 +1735,16 @@ static DecodeParams make_params(void* out, const void* query, const void* key_ca
   return p;
 }
 
-static void launch_decode_dt(const DecodeParams& p, int head_dim, int q_dtype, int kv_dtype, bool sh,
+static void launch_decode_dt(const DecodeParams& p, int head_dim, int q_dtype, int kv_dtype, bool sh, bool last,
                              hipStream_t st) {
   const bool bf = q_dtype == PKV_BF16;
   const bool f8 = kv_dtype == PKV_FP8_E4M3;
   if (head_dim == 128) {
-    if (f8) { if (bf) launch_decode<128, KFP8, true>(p, sh, st); else launch_decode<128, KFP8, false>(p, sh, st); }
-    else    { if (bf) launch_decode<128, KBF16, true>(p, sh, st); else launch_decode<128, KF16, false>(p, sh, st); }
+    if (f8) { if (bf) launch_decode<128, KFP8, true>(p, sh, last, st); else launch_decode<128, KFP8, false>(p, sh, last, st); }
+    else    { if (bf) launch_decode<128, KBF16, true>(p, sh, last, st); else launch_decode<128, KF16, false>(p, sh, last, st); }
   } else {
-    if (f8) { if (bf) launch_decode<64, KFP8, true>(p, sh, st); else launch_decode<64, KFP8, false>(p, sh, st); }
-    else    { if (bf) launch_decode<64, KBF16, true>(p, sh, st); else launch_decode<64, KF16, false>(p, sh, st); }
+    if (f8) { if (bf) launch_decode<64, KFP8, true>(p, sh, last, st); else launch_decode<64, KFP8, false>(p, sh, last, st); }
+    else    { if (bf) launch_decode<64, KBF16, true>(p, sh, last, st); else launch_decode<64, KF16, false>(p, sh, last, st); }
   }
 }
 
@@ -1712,6 +1755,7 @@ static int attn_entry(void* out, const void* query, const void* key_cache, const
                       int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
                       float k_scale, float v_scale, int max_context_len, int partition_size,
                       float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream) {
+  const TimedCall timed;
   const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
                             num_seqs, q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                             q_dtype, kv_dtype, k_scale, v_scale, max_context_len, partition_size, tmp_out,
@@ -1730,7 +1774,7 @@ static int attn_entry(void* out, const void* query, const void* key_cache, const
                                      num_seqs, q_len, num_heads, num_kv_heads, block_size, num_blocks, scale,
                                      k_scale, v_scale, max_context_len, partition_size, Pslots, tmp_out,
                                      max_logits, exp_sums);
-  launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, st);
+  launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, true, st);
   return launch_status();
 }
 
@@ -1764,6 +1808,7 @@ int paged_attn_decode_append(void* out, const void* query, const void* key, cons
                              int head_dim, int block_size, int num_blocks, float scale, int dtype,
                              int max_context_len, int partition_size, float* tmp_out, float* max_logits,
                              float* exp_sums, int flags, void* stream) {
+  const TimedCall timed;
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
   const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
                             num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
@@ -1797,10 +1842,10 @@ int paged_attn_decode_append(void* out, const void* query, const void* key, cons
     }
   } else {
     // other schedules: the append scatter, then the decode
-    hipLaunchKernelGGL(kv_append_kernel, dim3(num_seqs), dim3(256), 0, st, key, value, key_cache, value_cache,
-                       block_tables, context_lens, max_blocks, p.cap, (int)__builtin_ctz((unsigned)block_size),
-                       num_blocks, num_kv_heads * head_dim);
-    launch_decode_dt(p, head_dim, dtype, dtype, sh, st);
+    launch(kv_append_kernel, dim3(num_seqs), dim3(256), 0, st, false, key, value, key_cache, value_cache,
+           block_tables, context_lens, max_blocks, p.cap, (int)__builtin_ctz((unsigned)block_size), num_blocks,
+           num_kv_heads * head_dim);
+    launch_decode_dt(p, head_dim, dtype, dtype, sh, true, st);
   }
   return launch_status();
 }
@@ -1813,6 +1858,7 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
                                     int max_context_len, int prefix_len, int prefix_partition_size,
                                     int partition_size, float* tmp_out, float* max_logits, float* exp_sums,
                                     int flags, void* stream) {
+  const TimedCall timed;
   if (partition_size >= 0) return PKV_ERR_SHAPE;              // the suffix runs the balanced split
   const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
                             num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
@@ -1875,7 +1921,8 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
       else    { if (bf) launch_prefix<64, KBF16, true>(pp, st); else launch_prefix<64, KF16, false>(pp, st); }
     }
   }
-  if (Pslots > parts) launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, st);
+  if (Pslots > parts)
+    launch_decode_dt(p, head_dim, q_dtype, kv_dtype, (flags & PKV_FLAG_SHARED_BLOCKS) != 0, false, st);
   launch_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs, num_heads, head_dim, Pslots,
                 partition_size, p.cap, p.t0, parts, bf, st);
   return launch_status();
@@ -1907,6 +1954,7 @@ int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int p
 int paged_attn_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                       int max_context_len, int partition_size, int out_dtype, void* stream) {
+  const TimedCall timed;
   if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size == 0 ||
       partition_size < -(1 << 20))
     return PKV_ERR_SHAPE;

@@ -9,6 +9,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import paged_kv_cache_224_amd as pk
 from paged_kv_cache_224_amd import _lib
@@ -274,3 +275,90 @@ def test_swap_blocks_rejects(kw, want):
 def test_binding_raises_on_error_status():
     with pytest.raises(pk.PagedKVError):
         _lib._check("paged_attn_decode", E_SHAPE)
+
+
+# ---------------------------------------------------------------- binding-side validation
+# The binding checks every tensor against the shapes the kernels index with before calling the
+# library (shapes and dtypes first, the device last), so these run without a GPU.
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _decode_args(B=4, Hq=8, Hkv=2, D=64, BS=16, NB=80, maxlen=256, PS=-64, rows=None, P=None):
+    P = pk.lib().paged_attn_partial_slots(maxlen, PS) if P is None else P
+    rows = Hq if rows is None else rows
+    return dict(out=_t(B, Hq, D), query=_t(B, Hq, D), key_cache=_t(NB, BS, Hkv, D), value_cache=_t(NB, BS, Hkv, D),
+                block_tables=_t(B, 16, dtype=torch.int32), context_lens=_t(B, dtype=torch.int32), scale=0.125,
+                max_context_len=maxlen, partition_size=PS, tmp_out=_t(B, rows, P, D, dtype=torch.float32),
+                max_logits=_t(B, rows, P, dtype=torch.float32), exp_sums=_t(B, rows, P, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("change,match", [
+    (dict(tmp_out=_t(4, 8, 2, 64, dtype=torch.float32)), "tmp_out has shape"),      # workspace for a shorter max len
+    (dict(max_logits=_t(4, 8, 9, dtype=torch.float32)), "max_logits has shape"),    # another partition size
+    (dict(exp_sums=_t(4, 8, 17)), "exp_sums must be float32"),
+    (dict(tmp_out=_t(3, 8, 3, 64, dtype=torch.float32)), "tmp_out has shape"),      # fewer sequences
+    (dict(tmp_out=None), "tmp_out is required"),
+    (dict(out=_t(4, 8, 32)), "out has shape"),
+    (dict(out=_t(4, 8, 64, dtype=torch.float16)), "out has dtype"),
+    (dict(block_tables=_t(3, 16, dtype=torch.int32)), "block_tables must be"),      # fewer rows than sequences
+    (dict(context_lens=_t(2, dtype=torch.int32)), "context_lens must be"),
+    (dict(context_lens=_t(4, dtype=torch.int64)), "must be int32"),
+    (dict(value_cache=_t(80, 16, 2, 64, dtype=torch.float16)), "key_cache and value_cache"),
+    (dict(key_cache=_t(80, 16, 2, 64, dtype=torch.float16), value_cache=_t(80, 16, 2, 64, dtype=torch.float16)),
+     "cannot be read"),
+    (dict(key_cache=_t(80, 16, 2, 32), value_cache=_t(80, 16, 2, 32)), "head_dim differ"),
+    (dict(), "must be a GPU tensor"),                                                 # all shapes right: device last
+])
+def test_binding_validates_decode_arguments(change, match):
+    args = _decode_args()
+    args.update(change)
+    with pytest.raises(ValueError, match=match):
+        pk.paged_attn_decode(**args)
+
+
+def test_binding_accepts_a_workspace_for_a_larger_batch():
+    """A workspace sized for more sequences (the captured-graph buffers) passes the shape
+    checks; only the device check remains."""
+    args = _decode_args()
+    P = pk.lib().paged_attn_partial_slots(256, -64)
+    args.update(tmp_out=_t(9, 8, P, 64, dtype=torch.float32), max_logits=_t(9, 8, P, dtype=torch.float32),
+                exp_sums=_t(9, 8, P, dtype=torch.float32))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        pk.paged_attn_decode(**args)
+
+
+def test_binding_validates_multi_query_rows():
+    """Multi-query partials have q_len * num_heads rows per sequence."""
+    args = _decode_args(rows=8)                  # Hq rows: too few for q_len 2
+    args["query"] = _t(4, 2, 8, 64)
+    args["out"] = _t(4, 2, 8, 64)
+    with pytest.raises(ValueError, match="tmp_out has shape"):
+        pk.paged_attn_multi_query(**args)
+    args.update(_decode_args(rows=16))
+    args["query"] = _t(4, 2, 8, 64)
+    args["out"] = _t(4, 2, 8, 64)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        pk.paged_attn_multi_query(**args)
+
+
+def test_binding_validates_reduce_and_write():
+    P = pk.lib().paged_attn_partial_slots(256, 64)
+    good = dict(out=_t(4, 8, 64), tmp_out=_t(4, 8, P, 64, dtype=torch.float32),
+                max_logits=_t(4, 8, P, dtype=torch.float32), exp_sums=_t(4, 8, P, dtype=torch.float32),
+                context_lens=_t(4, dtype=torch.int32), max_context_len=256, partition_size=64)
+    with pytest.raises(ValueError, match="tmp_out has shape"):
+        pk.paged_attn_reduce(**{**good, "tmp_out": _t(4, 8, P - 1, 64, dtype=torch.float32)})
+    with pytest.raises(ValueError, match="context_lens must be"):
+        pk.paged_attn_reduce(**{**good, "context_lens": _t(5, dtype=torch.int32)})
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        pk.paged_attn_reduce(**good)
+    kv = dict(key=_t(3, 2, 64), value=_t(3, 2, 64), key_cache=_t(80, 16, 2, 64), value_cache=_t(80, 16, 2, 64),
+              slot_mapping=_t(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="slot_mapping has shape"):
+        pk.paged_kv_write(**{**kv, "slot_mapping": _t(2, dtype=torch.int64)})
+    with pytest.raises(ValueError, match="value has dtype"):
+        pk.paged_kv_write(**{**kv, "value": _t(3, 2, 64, dtype=torch.float16)})
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        pk.paged_kv_write(**kv)

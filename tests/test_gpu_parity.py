@@ -360,3 +360,34 @@ def test_checked_mode_rejects_bad_device_values(monkeypatch):
     monkeypatch.delenv("PKV_CHECK")
     pk.paged_attn_decode(*args)                    # fast path: clamped id, no fault
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- a caller error stays in its row
+
+@pytest.mark.parametrize("mode", ["balanced", "split", "single"])
+def test_length_past_the_table_spoils_only_its_row(mode):
+    """One context length above max_blocks * block_size (a caller error; PKV_CHECK=1 reports it)
+    must leave every other row correct: the decode and the reduce clamp lengths to the same
+    max_context_len, so they count the same split units, and the decode clamps the table index
+    to the row, so the bad row only re-reads its own last entry."""
+    cfg = I.shrink(I.CONFIGS["llama3_8b"], B=24, len_div=8, name="overlong")
+    _say(f"[overlong] {mode}")
+    w = I.make_workload(cfg)
+    kc_ref, vc_ref = oracle_pools(w)
+    ref = oracle_decode(w, kc_ref, vc_ref)
+    kc, vc = gpu_pools(w)
+    bad = 5
+    lens = w.context_lens.copy()
+    lens[bad] = cfg.max_blocks * cfg.block_size + 200
+    maxlen = int(lens.max())
+    PS = _partition(w, mode)
+    out = torch.full((cfg.B, cfg.Hq, cfg.D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = pk.DecodeWorkspace(cfg.B, cfg.Hq, cfg.D, maxlen, PS, device=DEV)
+    pk.decode(out, w.q.to(DEV), kc, vc, torch.from_numpy(w.block_tables).to(DEV), torch.from_numpy(lens).to(DEV),
+              w.scale, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    keep = np.arange(cfg.B) != bad
+    err = max_err(got[keep], ref[keep])
+    _say(f"    other rows max-abs err {err:.3e}")
+    assert err <= tolerance(cfg)
