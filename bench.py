@@ -13,6 +13,7 @@ the kernel's own dispatch on every timed step) and the fp64 CPU oracle timed on 
 cores (all of them, and one thread).
 """
 import argparse
+import ctypes
 import dataclasses
 import json
 import math
@@ -57,8 +58,8 @@ def parse():
     ap.add_argument("--event-every", type=int, default=1,
                     help="time the decode launch with HIP events on every N-th timed step (default: all)")
     ap.add_argument("--event-mode", default="kernel", choices=["kernel", "marker"],
-                    help="kernel: events bound to the call's kernels (pkv_time_next_call, no packet between "
-                         "kernels); marker: events recorded on the stream before and after the call")
+                    help="kernel: timing-only events bound to the call's kernels (pkv_time_next_call, no "
+                         "packet between kernels); marker: default events recorded on the stream around the call")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time to measure")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per pool copy)")
@@ -70,6 +71,43 @@ def parse():
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only copy a buffer of this size 5 times (reference for HBM traffic counters)")
     return ap.parse_args()
+
+
+class HipEvents:
+    """Timing-only HIP events created with hipEventDisableSystemFence: recording one skips the
+    system-scope cache write-back a default event performs, so timing every launch does not
+    slow the work that follows (a default event costs ~5 us per timed decode launch here)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                h = ctypes.c_void_p()
+                rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+                pair.append(h.value)
+            self.pairs.append(tuple(pair))
+
+    def elapsed_ms(self, pair):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(pair[0]), ctypes.c_void_p(pair[1]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for pair in self.pairs:
+            for h in pair:
+                self.hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.pairs = []
 
 
 def workload_cfg(args):
@@ -438,35 +476,47 @@ def main():
     torch.cuda.synchronize()
 
     marker = args.event_mode == "marker"
+    # Every call of the step is prepared once per pool copy (arguments validated and converted
+    # to C values by the binding), so the timed loop only makes the library calls.
+    def make_calls(kc, vc):
+        """The step's calls on one pool copy, prepared for the current stream."""
+        c = {}
+        if append:                                      # write + decode in one launch, then the merge
+            c["attn"] = pk.paged_attn_decode_append(None, q, k_new, v_new, kc, vc, bt, lens, w.scale, maxlen, PS,
+                                                    ws.tmp_out, ws.max_logits, ws.exp_sums, shared_blocks=shared,
+                                                    bind=True)
+        else:
+            c["write"] = pk.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale, bind=True)
+            if cascade:                                 # three kernels: prefix, suffix, merge
+                c["attn"] = pk.decode_shared_prefix(out, q, kc, vc, bt, lens, w.scale, sws, w.k_scale, w.v_scale,
+                                                    bind=True)
+            else:
+                c["attn"] = pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS,
+                                                 ws.tmp_out, ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale,
+                                                 shared_blocks=shared, bind=True)
+        if PS != 0 and not cascade:
+            c["reduce"] = pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS,
+                                               bind=True)
+        return c
 
-    def timed(call, ev):
-        """Run the attention call; with ev, time it (kernel-bound events, or markers around it)."""
+    calls = [make_calls(kc, vc) for kc, vc in pools]
+
+    def run_calls(c, ev=None):
+        if "write" in c:
+            c["write"]()
         if ev is not None:
             if marker:
                 ev[0].record()
             else:
                 pk.time_next_call(ev[0], ev[1])
-        call()
+        c["attn"]()
         if ev is not None and marker:
             ev[1].record()
+        if "reduce" in c:
+            c["reduce"]()
 
     def step(i, ev=None):
-        kc, vc = pools[i % copies]
-        if append:                                      # write + decode in one launch, then the merge
-            timed(lambda: pk.paged_attn_decode_append(None, q, k_new, v_new, kc, vc, bt, lens, w.scale, maxlen, PS,
-                                                      ws.tmp_out, ws.max_logits, ws.exp_sums, shared_blocks=shared),
-                  ev)
-            pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS)
-            return
-        pk.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
-        if cascade:                                     # three kernels: prefix, suffix, merge
-            timed(lambda: pk.decode_shared_prefix(out, q, kc, vc, bt, lens, w.scale, sws, w.k_scale, w.v_scale), ev)
-            return
-        timed(lambda: pk.paged_attn_decode(out if PS == 0 else None, q, kc, vc, bt, lens, w.scale, maxlen, PS,
-                                           ws.tmp_out, ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale,
-                                           shared_blocks=shared), ev)
-        if PS != 0:
-            pk.paged_attn_reduce(out, ws.tmp_out, ws.max_logits, ws.exp_sums, lens, maxlen, PS)
+        run_calls(calls[i % copies], ev)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -479,19 +529,25 @@ def main():
     # end), so no marker packet sits between two kernels of the step and the step rate is not
     # disturbed; --event-mode marker records them on the stream around the call instead.
     every = max(1, args.event_every)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if i % every == 0 else None
-           for i in range(args.steps)]
-    for e in evs:                                       # create the HIP events before the timed region
-        if e is not None:
-            e[0].record()
-            e[1].record()
+    nsamp = (args.steps + every - 1) // every
+    if marker:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if i % every == 0
+               else None for i in range(args.steps)]
+        elapsed = lambda e: e[0].elapsed_time(e[1])     # noqa: E731
+    else:
+        hip_events = HipEvents(nsamp)
+        it = iter(hip_events.pairs)
+        evs = [next(it) if i % every == 0 else None for i in range(args.steps)]
+        elapsed = hip_events.elapsed_ms
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    decode_ms = [e[0].elapsed_time(e[1]) for e in evs if e is not None]
+    decode_ms = [elapsed(e) for e in evs if e is not None]
+    if not marker:
+        hip_events.close()
 
     ms_per_step = 1e3 * wall / args.steps
 
@@ -503,7 +559,7 @@ def main():
         for c in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap_stream):
-                step(c)
+                run_calls(make_calls(*pools[c]))
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % copies].replay()
@@ -553,7 +609,8 @@ def main():
         "decode_kernel_ms_mean": round(dec_mean_ms, 5),
         "decode_kernel_ms_median": round(dec_median_ms, 5),
         "decode_event_samples": len(decode_ms),
-        "decode_event_mode": "bound to the kernels (hipExtLaunchKernel)" if not marker else "markers around the call",
+        "decode_event_mode": ("timing-only events bound to the kernels (hipExtLaunchKernel)" if not marker
+                              else "default events recorded around the call"),
         "decode_kernel_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(decode_ms, [10, 50, 90])],
         "step_bytes": {"logical": step_bytes_logical, "unique": step_bytes_unique},
         "roofline": {

@@ -101,11 +101,37 @@ def status_string(status: int) -> str:
     return lib().pkv_status_string(int(status)).decode()
 
 
-def time_next_call(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
-    """Bind two recorded timing events to the next attention call's kernels on this thread
-    (pkv_time_next_call): afterwards start.elapsed_time(stop) is that call's GPU time.  The
-    events must have been recorded once, so that their HIP events exist."""
-    lib().pkv_time_next_call(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+def time_next_call(start, stop) -> None:
+    """Bind two timing events (raw hipEvent_t handles as ints, or torch.cuda.Events that have
+    been recorded once so that their HIP events exist) to the next attention call's kernels on
+    this thread (pkv_time_next_call): the elapsed time between them is that call's GPU time."""
+    h = [e if isinstance(e, int) else e.cuda_event for e in (start, stop)]
+    lib().pkv_time_next_call(ctypes.c_void_p(h[0]), ctypes.c_void_p(h[1]))
+
+
+class BoundCall:
+    """A library call with its arguments validated and converted to C values once; calling it
+    repeats exactly that call (same tensors, same stream) with no per-call Python checks.  For
+    tight loops such as a benchmark's timed region."""
+
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name: str, args: tuple):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        self.args = tuple(None if a is None else t(a) for t, a in zip(self.fn.argtypes, args))
+
+    def __call__(self) -> None:
+        rc = self.fn(*self.args)
+        if rc != 0:
+            _check(self.name, rc)
+
+
+def _call(name: str, args: tuple, bind: bool):
+    """Call the library now, or (bind=True) return the prepared call."""
+    if bind:
+        return BoundCall(name, args)
+    _check(name, getattr(lib(), name)(*args))
 
 
 def _check(fn: str, status: int) -> None:
@@ -201,7 +227,7 @@ def _stream(stream) -> Optional[int]:
 
 def paged_kv_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                    value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
-                   v_scale: float = 1.0, stream=None) -> None:
+                   v_scale: float = 1.0, stream=None, bind: bool = False):
     """Scatter key/value [T, Hkv, D] into caches [NB, BS, Hkv, D] at slot_mapping [T] (int64).
 
     A uint8 / float8_e4m3fn cache is written as E4M3FN codes of x / scale."""
@@ -214,10 +240,9 @@ def paged_kv_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     _shape("value", value, key.shape, key.dtype)
     _shape("slot_mapping", slot_mapping, (T,), torch.int64)
     _on_gpu(key=key, value=value, key_cache=key_cache, value_cache=value_cache, slot_mapping=slot_mapping)
-    rc = lib().paged_kv_write(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+    return _call("paged_kv_write", (_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                               _ptr(slot_mapping), T, NB, BS, Hkv, D, _DT[key.dtype], _DT[key_cache.dtype],
-                              float(k_scale), float(v_scale), _stream(stream))
-    _check("paged_kv_write", rc)
+                              float(k_scale), float(v_scale), _stream(stream)), bind)
 
 
 def partial_slots(max_context_len: int, partition_size: int) -> int:
@@ -245,7 +270,7 @@ def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cach
                       scale: float, max_context_len: int, partition_size: int = 0,
                       tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
                       exp_sums: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
-                      stream=None, shared_blocks: bool = False) -> None:
+                      stream=None, shared_blocks: bool = False, bind: bool = False):
     """Decode attention; see include/pagedkv.h.  partition_size != 0 writes split-K partials.
     shared_blocks: some physical blocks appear in several table rows (keeps them cached)."""
     if query.dim() != 3:
@@ -261,13 +286,12 @@ def paged_attn_decode(out: Optional[torch.Tensor], query: torch.Tensor, key_cach
         _workspace(tmp_out, max_logits, exp_sums, B, Hq, partial_slots(max_context_len, partition_size), D)
     _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
             context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums)
-    rc = lib().paged_attn_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+    return _call("paged_attn_decode", (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv,
                                  D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
                                  float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
                                  _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
-                                 PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
-    _check("paged_attn_decode", rc)
+                                 PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream)), bind)
 
 
 def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key_cache: torch.Tensor,
@@ -275,7 +299,7 @@ def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key
                            scale: float, max_context_len: int, partition_size: int = 0,
                            tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
                            exp_sums: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0,
-                           stream=None, shared_blocks: bool = False) -> None:
+                           stream=None, shared_blocks: bool = False, bind: bool = False):
     """query [B, L, Hq, D]: L new tokens per sequence, causal among themselves (include/pagedkv.h).
     Split-K partials have L * Hq rows per sequence: tmp_out [B, L * Hq, P, D]."""
     if query.dim() != 4:
@@ -291,13 +315,12 @@ def paged_attn_multi_query(out: Optional[torch.Tensor], query: torch.Tensor, key
         _workspace(tmp_out, max_logits, exp_sums, B, Lq * Hq, partial_slots(max_context_len, partition_size), D)
     _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
             context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums)
-    rc = lib().paged_attn_multi_query(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+    return _call("paged_attn_multi_query", (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                       _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Lq, Hq,
                                       Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
                                       float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
                                       _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
-                                      PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
-    _check("paged_attn_multi_query", rc)
+                                      PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream)), bind)
 
 
 def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, context_lens, scale,
@@ -321,7 +344,7 @@ def paged_attn_decode_append(out: Optional[torch.Tensor], query: torch.Tensor, k
                              max_context_len: int, partition_size: int = 0,
                              tmp_out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
                              exp_sums: Optional[torch.Tensor] = None, stream=None,
-                             shared_blocks: bool = False) -> None:
+                             shared_blocks: bool = False, bind: bool = False):
     """Store key/value [B, Hkv, D] at position n - 1 of every sequence and decode, in one call
     (16-bit caches; include/pagedkv.h).  partition_size != 0 writes split-K partials."""
     if query.dim() != 3:
@@ -340,12 +363,11 @@ def paged_attn_decode_append(out: Optional[torch.Tensor], query: torch.Tensor, k
     _on_gpu(out=out, query=query, key=key, value=value, key_cache=key_cache, value_cache=value_cache,
             block_tables=block_tables, context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits,
             exp_sums=exp_sums)
-    rc = lib().paged_attn_decode_append(
+    return _call("paged_attn_decode_append", (
         _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype],
         int(max_context_len), int(partition_size), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
-        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
-    _check("paged_attn_decode_append", rc)
+        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream)), bind)
 
 
 def decode_append(out: torch.Tensor, query, key, value, key_cache, value_cache, block_tables, context_lens, scale,
@@ -366,7 +388,7 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_
                                     prefix_len: int, prefix_partition_size: int, partition_size: int,
                                     tmp_out: torch.Tensor, max_logits: torch.Tensor, exp_sums: torch.Tensor,
                                     k_scale: float = 1.0, v_scale: float = 1.0, stream=None,
-                                    shared_blocks: bool = False) -> None:
+                                    shared_blocks: bool = False, bind: bool = False):
     """Decode of a batch whose rows share their first prefix_len tokens' blocks: prefix pass,
     suffix pass and merge in one call; writes out [B, Hq, D] (include/pagedkv.h)."""
     if query.dim() != 3:
@@ -383,13 +405,12 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_
         _workspace(tmp_out, max_logits, exp_sums, B, Hq, P, D)
     _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
             context_lens=context_lens, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums)
-    rc = lib().paged_attn_decode_shared_prefix(
+    return _call("paged_attn_decode_shared_prefix", (
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
         float(k_scale), float(v_scale), int(max_context_len), int(prefix_len), int(prefix_partition_size),
         int(partition_size), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
-        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream))
-    _check("paged_attn_decode_shared_prefix", rc)
+        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream)), bind)
 
 
 def prefix_split(num_seqs: int, num_heads: int, num_kv_heads: int, prefix_len: int) -> int:
@@ -424,16 +445,16 @@ class SharedPrefixWorkspace:
 
 def decode_shared_prefix(out: torch.Tensor, query, key_cache, value_cache, block_tables, context_lens, scale,
                          ws: SharedPrefixWorkspace, k_scale=1.0, v_scale=1.0, stream=None,
-                         shared_blocks: bool = False) -> None:
-    paged_attn_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                                    ws.max_context_len, ws.prefix_len, ws.prefix_partition_size,
-                                    ws.partition_size, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale, v_scale,
-                                    stream, shared_blocks)
+                         shared_blocks: bool = False, bind: bool = False):
+    return paged_attn_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                                           ws.max_context_len, ws.prefix_len, ws.prefix_partition_size,
+                                           ws.partition_size, ws.tmp_out, ws.max_logits, ws.exp_sums, k_scale,
+                                           v_scale, stream, shared_blocks, bind)
 
 
 def paged_attn_reduce(out: torch.Tensor, tmp_out: torch.Tensor, max_logits: torch.Tensor,
                       exp_sums: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                      partition_size: int, stream=None) -> None:
+                      partition_size: int, stream=None, bind: bool = False):
     """Log-sum-exp merge of split-K partials into out [B, Hq, D]."""
     if out.dim() != 3 or out.dtype not in _KV16:
         raise ValueError("out must be float16/bfloat16 [num_seqs, num_heads, head_dim]")
@@ -442,10 +463,9 @@ def paged_attn_reduce(out: torch.Tensor, tmp_out: torch.Tensor, max_logits: torc
         raise ValueError(f"context_lens must be int32 [{B}]")
     _workspace(tmp_out, max_logits, exp_sums, B, Hq, partial_slots(max_context_len, partition_size), D)
     _on_gpu(out=out, tmp_out=tmp_out, max_logits=max_logits, exp_sums=exp_sums, context_lens=context_lens)
-    rc = lib().paged_attn_reduce(_ptr(out), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+    return _call("paged_attn_reduce", (_ptr(out), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
                                  _ptr(context_lens), B, Hq, D, int(max_context_len), int(partition_size),
-                                 _DT[out.dtype], _stream(stream))
-    _check("paged_attn_reduce", rc)
+                                 _DT[out.dtype], _stream(stream)), bind)
 
 
 def paged_attn_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
