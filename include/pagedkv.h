@@ -65,7 +65,8 @@ typedef enum {
   PKV_ERR_STATE = -8,      /* block manager: sequence id in use, or sequence in the wrong state */
   PKV_ERR_NOT_FOUND = -9,  /* block manager: unknown sequence id */
   PKV_ERR_NO_SPACE = -10,  /* block manager: not enough free blocks */
-  PKV_ERR_HOST = -11       /* a host buffer is not pinned, device-mapped memory of the needed size */
+  PKV_ERR_HOST = -11,      /* a host buffer is not pinned, device-mapped memory of the needed size */
+  PKV_ERR_SCRATCH = -12    /* paged_attn_decode_noalloc: the call needs more than the fixed scratch */
 } pkv_status;
 
 /* Flags of the attention calls. */
@@ -185,6 +186,35 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                            int block_size, int num_blocks, float scale, int q_dtype, int kv_dtype,
                            float k_scale, float v_scale, int max_context_len, int partition_size,
                            float* tmp_out, float* max_logits, float* exp_sums, int flags, void* stream);
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode followed by paged_attn_reduce in one call that
+ * allocates nothing and takes no workspace: for callers that cannot call hipMalloc or own a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid device
+ * allocation).  It writes the same `out` as that pair of calls, bit for bit.
+ *
+ *   partition_size  0: single pass (no partials).  < 0: the balanced split over W =
+ *                   -partition_size workgroups (paged_attn_balanced_split()), with the split-K
+ *                   partials kept in the library's own fixed device buffer (`scratch`, 32 MiB,
+ *                   one per GPU the library runs on, held until the process ends).  > 0 is
+ *                   PKV_ERR_SHAPE.
+ *   out             [num_seqs, num_heads, head_dim], q_dtype; always written.
+ * Scratch need of a balanced call: (num_seqs + Weff - 1) * num_heads * (head_dim + 2) * 4 bytes,
+ * Weff = max(1, min(W, num_seqs * (ceil(max_context_len / 16) + 1) / 8)); a call that needs more
+ * than 32 MiB returns PKV_ERR_SCRATCH before any launch (e.g. 12.7 MB for 128 sequences x 64
+ * heads x head_dim 128 at W = 256).
+ * Every call on one GPU shares that GPU's buffer and leaves its partials there: calls that
+ * overlap on one GPU (different streams, or other threads) race and give unspecified results;
+ * calls ordered on one stream are safe.  The first call on a device looks up the buffer's
+ * address (hipGetSymbolAddress) and keeps it; no call allocates, frees or synchronises.
+ * PKV_CHECK=1 is not honoured here (checking would copy to host memory).  Every other argument,
+ * the supported set and the error behaviour are those of paged_attn_decode.
+ */
+int paged_attn_decode_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
+                              float v_scale, int max_context_len, int partition_size, int flags, void* stream);
 
 /*
  * paged_attn_decode_append -- one decode step in one call for 16-bit caches: the step's new
@@ -389,7 +419,8 @@ int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int p
  * pkv_time_next_call -- measurement hook.  Binds two caller-owned HIP events (hipEvent_t,
  * created with timing enabled) to the kernels of the NEXT attention call made on the calling
  * thread (paged_attn_decode, paged_attn_multi_query, paged_attn_decode_append,
- * paged_attn_decode_shared_prefix or paged_attn_reduce): `start_event` is recorded when that
+ * paged_attn_decode_shared_prefix, paged_attn_decode_noalloc or paged_attn_reduce):
+ * `start_event` is recorded when that
  * call's first kernel starts and `stop_event` when its last kernel ends (hipExtLaunchKernel),
  * so hipEventElapsedTime(start, stop) is the call's GPU execution time with no marker packet
  * between kernels.  One-shot: the next attention call consumes the events whether or not it

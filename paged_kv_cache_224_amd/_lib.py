@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_ERR_SHAPE = -2
+PKV_ERR_SCRATCH = -12
 PKV_FLAG_SHARED_BLOCKS = 1
 _DT = {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3,
        torch.float8_e4m3fn: PKV_FP8_E4M3}
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_multi_query.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, I, F, F, I, I, P, P,
                                              P, I, P]
         L.paged_attn_multi_query.restype = I
+        L.paged_attn_decode_noalloc.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, F, F, I, I, I, P]
+        L.paged_attn_decode_noalloc.restype = I
         L.paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         L.paged_attn_reduce.restype = I
         L.paged_attn_decode_append.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F, I, I, I, P, P, P,
@@ -336,6 +339,30 @@ def multi_query(out: torch.Tensor, query, key_cache, value_cache, block_tables, 
     if PS != 0:
         paged_attn_reduce(out.view(B, Lq * Hq, D), ws.tmp_out, ws.max_logits, ws.exp_sums, context_lens,
                           ws.max_context_len, PS, stream)
+
+
+def paged_attn_decode_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                              value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                              scale: float, max_context_len: int, partition_size: int = 0, k_scale: float = 1.0,
+                              v_scale: float = 1.0, stream=None, shared_blocks: bool = False, bind: bool = False):
+    """Decode (and, for partition_size < 0, the merge) with the split-K partials in the
+    library's fixed device scratch: no workspace, no allocation (include/pagedkv.h).  Calls that
+    overlap on one GPU race on that scratch."""
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_heads, head_dim]")
+    B, Hq, D = query.shape
+    NB, BS, Hkv, D2 = _pools(query.dtype, key_cache, value_cache)
+    if D2 != D:
+        raise ValueError("query and cache head_dim differ")
+    _tables(block_tables, context_lens, B)
+    _shape("out", out, query.shape, query.dtype)
+    _on_gpu(out=out, query=query, key_cache=key_cache, value_cache=value_cache, block_tables=block_tables,
+            context_lens=context_lens)
+    return _call("paged_attn_decode_noalloc", (
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, Hq, Hkv, D, BS, NB, float(scale), _DT[query.dtype], _DT[key_cache.dtype],
+        float(k_scale), float(v_scale), int(max_context_len), int(partition_size),
+        PKV_FLAG_SHARED_BLOCKS if shared_blocks else 0, _stream(stream)), bind)
 
 
 def paged_attn_decode_append(out: Optional[torch.Tensor], query: torch.Tensor, key: torch.Tensor,

@@ -46,6 +46,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -254,6 +255,9 @@ struct DecodeParams {
   int t0;          // balanced split: tiles skipped at the start of every sequence (a shared
                    // prefix handled elsewhere); the stream holds tiles [t0, ceil(n / 16))
   int slot0;       // partial slots below slot0 belong to someone else (the prefix pass)
+  int compact;     // balanced split, partials in the compact layout: the overlap of sequence b with
+                   // workgroup w is partial b + w (unique: overlaps are ordered in both b and w), so
+                   // a row needs B + W - 1 slots, [B + W - 1][L * Hq] partials in all
   int tile_shift;  // log2(BS / 16)
   float c2;        // scale * k_scale * log2(e)
   float v_scale;
@@ -709,8 +713,9 @@ void pa_decode_kernel(DecodeParams a) {
           wv.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
           *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
         }
-      } else if (sg.slot >= 0 && a.slot0 + sg.slot < a.Pslots) {
-        const size_t prow = (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * a.Pslots + a.slot0 + sg.slot;
+      } else if (sg.slot >= 0 && (a.compact || a.slot0 + sg.slot < a.Pslots)) {
+        const size_t prow = a.compact ? (size_t)(sg.b + src.w) * a.L * a.Hq + (size_t)qi * a.Hq + hoff
+                                      : (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * a.Pslots + a.slot0 + sg.slot;
         float* orow = a.tmp_out + prow * D;
 #pragma unroll
         for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
@@ -1234,16 +1239,17 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
 // partials of fixed partitions, P = ceil(n / PS).  PS < 0: balanced split over -PS
 // workgroups; P = number of ranges the sequence's tiles (past its first t0) fall in,
 // recomputed from the lengths exactly as the decode did.  slot0 leading slots (a shared
-// prefix's partials) come before those P.  No LDS and no barrier: 16-lane row r of the wave folds the
-// partials p = r, r+4, ... into a running (max, weight sum, weighted o) over its D/16 output
-// elements per lane, and the four rows are combined with permlane swaps.
+// prefix's partials) come before those P.  compact: the balanced split's compact layout (partial
+// b + w of row h sits at [b + w][h]; see DecodeParams).  No LDS and no barrier: 16-lane row r of
+// the wave folds the partials p = r, r+4, ... into a running (max, weight sum, weighted o) over
+// its D/16 output elements per lane, and the four rows are combined with permlane swaps.
 template <int D, bool BF>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* tmp_out,
                                                        const float* max_logits,
                                                        const float* exp_sums,
                                                        const int32_t* lens, int B, int Hq,
                                                        int Pslots, int PS, int cap, int t0,
-                                                       int slot0) {
+                                                       int slot0, int compact) {
   constexpr int DPL = D / 16;                 // output elements per lane (8 or 4)
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, l16 = lane & 15;
@@ -1251,7 +1257,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
   if (row >= B * Hq) return;
   const int b = row / Hq;
   const int n = clamp_len(__builtin_amdgcn_readfirstlane(lens[b]), cap);
-  int P;
+  int P, first_range = 0;
   if (PS > 0) {
     P = (n + PS - 1) / PS;
   } else {
@@ -1270,10 +1276,11 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
     } else {
       const Split split(total, -PS);
       const int first = before + 1;          // the unit of b's first tile
-      P = split.owner(first + nt - 1) - split.owner(first) + 1;
+      first_range = split.owner(first);
+      P = split.owner(first + nt - 1) - first_range + 1;
     }
   }
-  P = min(slot0 + P, Pslots);
+  if (!compact) P = min(slot0 + P, Pslots);
   unsigned short* orow = (unsigned short*)out + (size_t)row * D + l16 * DPL;
   if (P == 0) {
     if (grp == 0) {
@@ -1284,9 +1291,12 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
     }
     return;
   }
-  const float* ml = max_logits + (size_t)row * Pslots;
-  const float* es = exp_sums + (size_t)row * Pslots;
-  const float* to = tmp_out + (size_t)row * Pslots * D + l16 * DPL;
+  // partial p of this row: index base + p * pstride of max_logits / exp_sums (times D for tmp_out)
+  const size_t base = compact ? (size_t)(b + first_range) * Hq + (row - b * Hq) : (size_t)row * Pslots;
+  const size_t pstride = compact ? (size_t)Hq : 1;
+  const float* ml = max_logits + base;
+  const float* es = exp_sums + base;
+  const float* to = tmp_out + base * D + l16 * DPL;
 
   float acc[DPL];
 #pragma unroll
@@ -1294,12 +1304,12 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
   float mrun = -INFINITY, wrun = 0.f;
 #pragma unroll 4
   for (int p = grp; p < P; p += 4) {
-    const float mp = ml[p] * kLog2e;
-    const float lp = es[p];
+    const float mp = ml[p * pstride] * kLog2e;
+    const float lp = es[p * pstride];
     float o[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; i += 4) {
-      const f32x4 v = *(const f32x4*)(to + (size_t)p * D + i);
+      const f32x4 v = *(const f32x4*)(to + p * pstride * D + i);
       o[i] = v[0];
       o[i + 1] = v[1];
       o[i + 2] = v[2];
@@ -1494,13 +1504,13 @@ void launch_prefix(const PrefixParams& p, hipStream_t st) {
 
 void launch_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                    const int32_t* lens, int B, int rows_per_seq, int D, int Pslots, int PS, int cap,
-                   int t0, int slot0, bool bf, hipStream_t st) {
+                   int t0, int slot0, bool bf, hipStream_t st, int compact = 0) {
   const dim3 grid((unsigned)(((long long)B * rows_per_seq + 3) / 4)), block(256);
   const int Pm = Pslots > 0 ? Pslots : 1;
   auto k = D == 128 ? (bf ? pa_reduce_kernel<128, true> : pa_reduce_kernel<128, false>)
                     : (bf ? pa_reduce_kernel<64, true> : pa_reduce_kernel<64, false>);
   launch(k, grid, block, 0, st, true, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0,
-         slot0);
+         slot0, compact);
 }
 
 // Partial slots of a shared-prefix decode: the prefix partitions first, then the balanced
@@ -1526,6 +1536,35 @@ int occupancy_blocks(int Hkv) {
 
 }  // namespace
 
+// ------------------------------------------------------------------ fixed scratch (no allocation)
+
+// Split-K partials of paged_attn_decode_noalloc: a fixed device array, one copy per GPU the
+// library runs on, held until the process ends.  Host code never uses its name as an address
+// (that is a host-side stand-in); the device address comes from hipGetSymbolAddress, once per
+// device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PKV_ERR_LAUNCH;
+    scratch_dev[dev] = ptr;
+  }
+  *out = scratch_dev[dev];
+  return PKV_OK;
+}
+}  // namespace
+
 // ==================================================================== C ABI
 
 extern "C" {
@@ -1544,6 +1583,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_NOT_FOUND: return "unknown sequence id";
     case PKV_ERR_NO_SPACE: return "not enough free blocks";
     case PKV_ERR_HOST: return "host buffer is not pinned, mapped host memory of the required size";
+    case PKV_ERR_SCRATCH: return "the call needs more scratch than the library's fixed device buffer holds";
     default: return "unknown status";
   }
 }
@@ -1730,6 +1770,7 @@ static DecodeParams make_params(void* out, const void* query, const void* key_ca
   p.v_scale = v_scale;
   p.t0 = 0;
   p.slot0 = 0;
+  p.compact = 0;
   p.knew = nullptr;
   p.vnew = nullptr;
   return p;
@@ -1800,6 +1841,50 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                     q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, q_dtype,
                     kv_dtype, k_scale, v_scale, max_context_len, partition_size, tmp_out, max_logits,
                     exp_sums, flags, stream);
+}
+
+int paged_attn_decode_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float scale, int q_dtype, int kv_dtype, float k_scale,
+                              float v_scale, int max_context_len, int partition_size, int flags, void* stream) {
+  const TimedCall timed;
+  if (partition_size > 0 || partition_size < -(1 << 20)) return PKV_ERR_SHAPE;
+  // the argument checks of the single pass (out is always written here)
+  const int rc = check_attn(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens, num_seqs,
+                            1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, q_dtype, kv_dtype,
+                            k_scale, v_scale, max_context_len, 0, nullptr, nullptr, nullptr, flags);
+  if (rc != PKV_OK) return rc > 0 ? PKV_OK : rc;
+  hipStream_t st = (hipStream_t)stream;
+  const bool sh = (flags & PKV_FLAG_SHARED_BLOCKS) != 0;
+  if (partition_size == 0) {                                  // single pass: no partials
+    const DecodeParams p = make_params(out, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                                       num_seqs, 1, num_heads, num_kv_heads, block_size, num_blocks, scale, k_scale,
+                                       v_scale, max_context_len, 0, 0, nullptr, nullptr, nullptr);
+    launch_decode_dt(p, head_dim, q_dtype, kv_dtype, sh, true, st);
+    return launch_status();
+  }
+  // Balanced split, partials in the compact layout: at most B + Weff - 1 slots per head, where
+  // Weff <= min(W, units / kMinChunkTiles) and units <= B * (ceil(max_len / 16) + 1).
+  const long long units = (long long)num_seqs * ((max_context_len + 15) / 16 + 1);
+  const long long weff = std::max(1LL, std::min((long long)-partition_size, units / kMinChunkTiles));
+  const long long rows = (num_seqs + weff - 1) * (long long)num_heads;
+  const long long need = rows * (head_dim + 2) * (long long)sizeof(float);
+  if (need > (long long)kScratchBytes) return PKV_ERR_SCRATCH;
+  void* base = nullptr;
+  const int sr = scratch_address(&base);
+  if (sr != PKV_OK) return sr;
+  float* tmp = (float*)base;                                  // [rows][D], then [rows] twice
+  float* ml = tmp + rows * head_dim;
+  float* es = ml + rows;
+  DecodeParams p = make_params(nullptr, query, key_cache, value_cache, block_tables, max_blocks, context_lens,
+                               num_seqs, 1, num_heads, num_kv_heads, block_size, num_blocks, scale, k_scale, v_scale,
+                               max_context_len, partition_size, 0, tmp, ml, es);
+  p.compact = 1;
+  if (max_context_len > 0) launch_decode_dt(p, head_dim, q_dtype, kv_dtype, sh, false, st);
+  launch_reduce(out, tmp, ml, es, context_lens, num_seqs, num_heads, head_dim, 1, partition_size, p.cap, 0, 0,
+                q_dtype == PKV_BF16, st, 1);
+  return launch_status();
 }
 
 int paged_attn_decode_append(void* out, const void* query, const void* key, const void* value,

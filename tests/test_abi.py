@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
                           "paged_attn_shared_prefix_slots", "paged_attn_prefix_split",
                           "paged_kv_swap_blocks", "pkv_bm_create", "pkv_bm_append", "pkv_bm_check",
                           "paged_attn_workspace_bytes", "paged_attn_partial_slots",
-                          "paged_attn_balanced_split", "pkv_status_string"}
+                          "paged_attn_balanced_split", "pkv_status_string", "paged_attn_decode_noalloc",
+                          "pkv_time_next_call"}
     L = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert pk.status_string(0) == "ok"
-    for s in range(-11, 0):
+    for s in range(-12, 0):
         assert pk.status_string(s) not in ("ok", "unknown status")
     assert pk.status_string(-99) == "unknown status"
 
@@ -362,3 +363,29 @@ def test_binding_validates_reduce_and_write():
         pk.paged_kv_write(**{**kv, "value": _t(3, 2, 64, dtype=torch.float16)})
     with pytest.raises(ValueError, match="must be a GPU tensor"):
         pk.paged_kv_write(**kv)
+
+
+def _noalloc(**kw):
+    args = dict(out=A, q=A, kc=A, vc=A, bt=A, max_blocks=16, lens=A, B=4, Hq=8, Hkv=2, D=64, BS=16, NB=80,
+                scale=0.125, qdt=0, kvdt=0, ks=1.0, vs=1.0, maxlen=256, PS=-64, flags=0, stream=None)
+    args.update(kw)
+    return pk.lib().paged_attn_decode_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(PS=512), E_SHAPE),                   # fixed partitions have no compact layout here
+    (dict(PS=-(1 << 21)), E_SHAPE),
+    (dict(out=None), E_NULL),                  # the merged output is always written
+    (dict(q=None), E_NULL),
+    (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(qdt=0, kvdt=1), E_DTYPE),
+    (dict(kc=MIS), E_ALIGN),
+    # (4096 + 255) x 32 heads x (128 + 2) x 4 bytes of partials > the 32 MiB scratch
+    (dict(B=4096, Hq=32, Hkv=8, D=128, maxlen=128), -12),
+])
+def test_noalloc_rejects(kw, want):
+    assert _noalloc(**kw) == want
+
+
+def test_noalloc_zero_sequences_is_a_noop():
+    assert _noalloc(B=0, q=None, out=None) == OK
