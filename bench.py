@@ -313,9 +313,11 @@ def device_pools(w, dev, copies=None):
 
 def multi_query_op(args):
     """L new tokens per sequence (speculative verification / chunked prefill) on the workload's
-    batch: the multi-query kernel timed by HIP events, the whole call (kernel + reduce) by wall
-    clock.  Algorithmic bytes: the KV rows once (shared by the L tokens), L query rows and L
-    output rows per (sequence, head), the used table entries and lengths."""
+    batch, balanced split of paged_attn_multi_query_split(): the attention call timed by
+    kernel-bound events on every step, the whole step (attention + merge) by wall clock.
+    Algorithmic bytes: the KV rows once (shared by the L tokens), L query rows and L output rows
+    per (sequence, head), the used table entries and lengths.  Flops: 4 * D per (query row,
+    visible token), QK^T and PV; new token i of a sequence sees n - L + 1 + i tokens."""
     dev = torch.device("cuda:0")
     cfg = workload_cfg(args)
     L = args.q_len
@@ -325,36 +327,48 @@ def multi_query_op(args):
     q = I.multi_query_q(cfg, L, 0).to(dev)
     bt = torch.from_numpy(w.block_tables).to(dev)
     lens = torch.from_numpy(w.context_lens).to(dev)
-    PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], torch.uint8 if fp8 else I.DTYPES[cfg.kv_dtype])
+    kvdt = torch.uint8 if fp8 else I.DTYPES[cfg.kv_dtype]
+    PS = args.partition_size if args.partition_size is not None else \
+        pk.multi_query_split(cfg.Hq, cfg.Hkv, cfg.D, L, I.DTYPES[cfg.q_dtype], kvdt)
     ws = pk.DecodeWorkspace(cfg.B, L * cfg.Hq, cfg.D, cfg.max_len, PS, device=dev)
     out = torch.empty((cfg.B, L, cfg.Hq, cfg.D), dtype=I.DTYPES[cfg.q_dtype], device=dev)
     shared = bool(w.prefix_blocks.size)                 # tables share a common prefix's blocks
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    calls = [pk.paged_attn_multi_query(None if PS else out, q, kc, vc, bt, lens, w.scale, cfg.max_len, PS,
+                                       ws.tmp_out, ws.max_logits, ws.exp_sums, w.k_scale, w.v_scale,
+                                       shared_blocks=shared, bind=True) for kc, vc in pools]
+    merge = pk.paged_attn_reduce(out.view(cfg.B, L * cfg.Hq, cfg.D), ws.tmp_out, ws.max_logits, ws.exp_sums,
+                                 lens, cfg.max_len, PS, bind=True) if PS else None
+    hev = HipEvents(args.steps)
 
     def run(i, e=None):
-        kc, vc = pools[i % copies]
         if e is not None:
-            e[0].record()
-        pk.paged_attn_multi_query(None, q, kc, vc, bt, lens, w.scale, cfg.max_len, PS, ws.tmp_out, ws.max_logits,
-                                  ws.exp_sums, w.k_scale, w.v_scale, shared_blocks=shared)
-        if e is not None:
-            e[1].record()
-        pk.paged_attn_reduce(out.view(cfg.B, L * cfg.Hq, cfg.D), ws.tmp_out, ws.max_logits, ws.exp_sums, lens,
-                             cfg.max_len, PS)
+            pk.time_next_call(e[0], e[1])
+        calls[i % copies]()
+        if merge is not None:
+            merge()
 
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run(i, ev[i])
+        run(i, hev.pairs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    kern_ms = [hev.elapsed_ms(p) for p in hev.pairs]
+    hev.close()
+    kern = float(np.mean(kern_ms)) * 1e-3
     nb = I.algorithmic_bytes(w)
     e_q = 2
     moved = nb["kv_unique"] + 2 * L * cfg.B * cfg.Hq * cfg.D * e_q + 4 * int(w.blocks_used.sum()) + 4 * cfg.B
+    n = w.context_lens.astype(np.int64)
+    visible = sum(int(np.clip(n - L + 1 + i, 0, None).sum()) for i in range(L))
+    flops = 4 * cfg.D * cfg.Hq * visible
     gbps = moved / kern / 1e9
+    tflops = flops / kern / 1e12
+    mfma_peak = 2500.0                                  # dense bf16 / f16 MFMA, TFLOP/s
+    hbm_frac, mfma_frac = gbps / HBM_PEAK_GBPS, tflops / mfma_peak
+    tiled = cfg.group * L > 16
     res = {"metric": "multi-query paged attention KV GB/s and query tokens/s", "value": round(gbps, 1),
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -362,8 +376,15 @@ def multi_query_op(args):
            "config": {"workload": cfg.name, "q_len": L, "num_seqs": cfg.B, "num_heads": cfg.Hq,
                       "num_kv_heads": cfg.Hkv, "head_dim": cfg.D, "partition_size": PS},
            "query_tokens_per_s": round(cfg.B * L / wall, 1), "kernel_ms_mean": round(kern * 1e3, 5),
-           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_decode_kernel",
+           "kernel_ms_median": round(float(np.median(kern_ms)), 5), "kernel_samples": len(kern_ms),
+           "tflops": round(tflops, 1), "flops_per_launch": flops,
+           "roofline": {"bound": "hbm" if hbm_frac >= mfma_frac else "mfma",
+                        "achieved": round(gbps if hbm_frac >= mfma_frac else tflops, 1),
+                        "peak": HBM_PEAK_GBPS if hbm_frac >= mfma_frac else mfma_peak,
+                        "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
+                        "frac": round(max(hbm_frac, mfma_frac), 4), "hbm_frac": round(hbm_frac, 4),
+                        "mfma_frac": round(mfma_frac, 4), "traffic": None,
+                        "kernel": "pa_mq_tiled_kernel" if tiled else "pa_decode_kernel",
                         "bytes_per_launch": moved}}
     print(json.dumps(res), flush=True)
 

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_workspace_bytes.restype = ctypes.c_size_t
         L.paged_attn_partial_slots.argtypes = [I, I]
         L.paged_attn_partial_slots.restype = I
+        L.paged_attn_multi_query_split.argtypes = [I, I, I, I, I, I]
+        L.paged_attn_multi_query_split.restype = I
         L.paged_attn_balanced_split.argtypes = [I, I, I, I]
         L.paged_attn_balanced_split.restype = I
         L.pkv_time_next_call.argtypes = [P, P]
@@ -265,6 +267,17 @@ def balanced_split(num_kv_heads: int, head_dim: int, q_dtype: torch.dtype, kv_dt
     v = int(lib().paged_attn_balanced_split(num_kv_heads, head_dim, _DT[q_dtype], _DT[kv_dtype]))
     if v >= 0:
         raise PagedKVError("paged_attn_balanced_split", v, "no device / unsupported shape")
+    return v
+
+
+def multi_query_split(num_heads: int, num_kv_heads: int, head_dim: int, q_len: int, q_dtype: torch.dtype,
+                      kv_dtype: torch.dtype) -> int:
+    """partition_size value (< 0) of the balanced split that fills the current device for
+    paged_attn_multi_query with q_len new tokens per sequence."""
+    v = int(lib().paged_attn_multi_query_split(num_heads, num_kv_heads, head_dim, q_len, _DT[q_dtype],
+                                               _DT[kv_dtype]))
+    if v >= 0:
+        raise PagedKVError("paged_attn_multi_query_split", v, "no device / unsupported shape")
     return v
 
 

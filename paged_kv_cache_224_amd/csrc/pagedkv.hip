@@ -129,6 +129,24 @@ __device__ __forceinline__ void fp8x16_to_16(u32x4 in, u32x4& lo, u32x4& hi) {
   hi.w = fp8x2_to_16<BF, true>(in.w);
 }
 
+// A row of fp8 codes widened into LDS: the 16 codes of one 16-byte load become two 16-byte
+// chunks (2c, 2c + 1) of 16-bit values.  A 16-byte store is serviced eight lanes (128 bytes of
+// banks) at a time; if all eight stored their even chunk first, the chunk positions modulo 8
+// would take only four values (the swizzles are even) and every store would conflict two ways.
+// So lanes 4-7 of each group of eight (`flip`) store their odd chunk first: they swap the two
+// input halves before widening, and the caller passes the two addresses in that order.  The
+// layout and the reads are unchanged; only the order of the two stores differs between lanes.
+__device__ __forceinline__ bool fp8_store_flip(int lane_or_index) { return ((lane_or_index >> 2) & 1) != 0; }
+
+template <bool BF>
+__device__ __forceinline__ void fp8x16_store_lds(u32x4 in, bool flip, char* first_slot, char* second_slot) {
+  const u32x4 x = {flip ? in.z : in.x, flip ? in.w : in.y, flip ? in.x : in.z, flip ? in.y : in.w};
+  u32x4 a, b;
+  fp8x16_to_16<BF>(x, a, b);
+  *(u32x4*)first_slot = a;
+  *(u32x4*)second_slot = b;
+}
+
 template <bool BF>
 __device__ __forceinline__ unsigned short f32_to_16(float x) {  // round to nearest even
   if constexpr (BF)
@@ -409,6 +427,47 @@ struct SegSource {
   }
 };
 
+// Balanced split, the first segment of workgroup w out of W: every wave of the workgroup runs
+// this with the same result.  Scans the lengths (units_after: one unit per tile past t0, plus one
+// per sequence), cuts the unit stream into W ranges and positions `src` at the first sequence
+// of range w.  Returns false when the range holds no tile.
+__device__ __forceinline__ bool balanced_start(SegSource& src, Seg& cur, const int32_t* lens, int B, int cap,
+                                               int t0, int W, int w, int lane) {
+  src.mode = MODE_BALANCED;
+  src.B = B;
+  src.cap = cap;
+  src.lens = lens;
+  src.t0 = t0;
+  const int per = (B + 63) >> 6;                        // sequences per lane in the scan
+  int run = 0, n_first = 0;
+  for (int i = 0; i < per; ++i) {
+    const int bb = lane * per + i;
+    const int n = bb < B ? clamp_len(lens[bb], cap) : 0;
+    if (i == 0) n_first = n;
+    run += units_after(n, t0);
+  }
+  const int incl = wave_incl_scan(run);                 // inclusive scan over lanes
+  const int N = __builtin_amdgcn_readlane(incl, 63);
+  if (N == 0) return false;
+  const Split split(N, W);
+  if (w >= split.Weff) return false;
+  src.w = w;
+  src.split = split;
+  src.lo = split.lo(w);
+  src.hi = split.lo(w + 1);
+  if (per == 1) {
+    src.fill(0, 0, lane, n_first);                      // the scan already holds every length
+  } else {
+    // the lane whose run of sequences holds tile `lo` starts the table
+    const unsigned long long hit = __ballot(incl > src.lo);
+    if (hit == 0) return false;                         // unreachable for lo < N
+    const int L = __builtin_ctzll(hit);
+    src.fill_load(L * per, __builtin_amdgcn_readlane(incl - run, L), lane);
+  }
+  cur = src.from_lane(0, lane);
+  return cur.valid;
+}
+
 // One workgroup = up to kMaxWaves waves; wave i handles KV head g = blockIdx.y*kMaxWaves + i,
 // so the waves stream whole blocks ([BS][Hkv][D] is contiguous) together.  Each wave owns one
 // LDS tile and runs one continuous tile pipeline over all segments of its workgroup: the next
@@ -466,36 +525,7 @@ void pa_decode_kernel(DecodeParams a) {
     if (!cur.valid) return;
   } else {
     // MODE_BALANCED: equal contiguous ranges of the batch's (sequence, tile) stream
-    const int B = a.B;
-    const int per = (B + 63) >> 6;                      // sequences per lane in the scan
-    int run = 0, n_first = 0;
-    for (int i = 0; i < per; ++i) {
-      const int bb = lane * per + i;
-      const int n = bb < B ? clamp_len(a.lens[bb], cap) : 0;
-      if (i == 0) n_first = n;
-      run += units_after(n, src.t0);
-    }
-    const int incl = wave_incl_scan(run);               // inclusive scan over lanes
-    const int N = __builtin_amdgcn_readlane(incl, 63);
-    if (N == 0) return;
-    const Split split(N, a.W);
-    const int w = blockIdx.x;
-    if (w >= split.Weff) return;
-    src.w = w;
-    src.split = split;
-    src.lo = split.lo(w);
-    src.hi = split.lo(w + 1);
-    if (per == 1) {
-      src.fill(0, 0, lane, n_first);                    // the scan already holds every length
-    } else {
-      // the lane whose run of sequences holds tile `lo` starts the table
-      const unsigned long long hit = __ballot(incl > src.lo);
-      if (hit == 0) return;                             // unreachable for lo < N
-      const int L = __builtin_ctzll(hit);
-      src.fill_load(L * per, __builtin_amdgcn_readlane(incl - run, L), lane);
-    }
-    cur = src.from_lane(0, lane);
-    if (!cur.valid) return;
+    if (!balanced_start(src, cur, a.lens, a.B, cap, src.t0, a.W, blockIdx.x, lane)) return;
   }
   // Issue priority by progress (balanced split: every wave of the workgroup streams the same
   // tiles of its own head).  The sequencer favours a SIMD's older wave, so with equal priority
@@ -542,14 +572,16 @@ void pa_decode_kernel(DecodeParams a) {
   int voff[TL::VLD];
   int vslot[TL::VLD];    // LDS byte offset of the (first) 16-bit chunk this load fills
   int vslot2[TL::VLD];   // fp8 only: the second chunk (16 codes widen to 32 bytes)
+  const bool vflip = fp8_store_flip(lane);              // fp8: store order of the widened chunks
 #pragma unroll
   for (int r = 0; r < TL::VLD; ++r) {
     const int t = r * TL::TPI + lane / TL::CPRS;
     const int cs = lane % TL::CPRS;
     voff[r] = t * rowstride + cs * 16;
     if constexpr (KV == KFP8) {
-      vslot[r] = lds_slot<TL::CPR>(t, 2 * cs) * 16;
-      vslot2[r] = lds_slot<TL::CPR>(t, 2 * cs + 1) * 16;
+      // stored in this order (see fp8x16_store_lds)
+      vslot[r] = lds_slot<TL::CPR>(t, 2 * cs + (vflip ? 1 : 0)) * 16;
+      vslot2[r] = lds_slot<TL::CPR>(t, 2 * cs + (vflip ? 0 : 1)) * 16;
     } else {
       vslot[r] = lds_slot<TL::CPR>(t, cs) * 16;
       vslot2[r] = 0;
@@ -644,14 +676,10 @@ void pa_decode_kernel(DecodeParams a) {
     }
 #pragma unroll
     for (int r = 0; r < TL::VLD; ++r) {
-      if constexpr (KV == KFP8) {
-        u32x4 lo, hi;
-        fp8x16_to_16<BF>(vr[r], lo, hi);
-        *(u32x4*)(vtile + vslot[r]) = lo;
-        *(u32x4*)(vtile + vslot2[r]) = hi;
-      } else {
+      if constexpr (KV == KFP8)
+        fp8x16_store_lds<BF>(vr[r], vflip, vtile + vslot[r], vtile + vslot2[r]);
+      else
         *(u32x4*)(vtile + vslot[r]) = vr[r];
-      }
     }
     return s;
   };
@@ -873,57 +901,51 @@ void pa_decode_kernel(DecodeParams a) {
   }
 }
 
-// ------------------------------------------------------------------ shared-prefix pass
+// ------------------------------------------------------------------ tiled passes
 
-// When every row of a batch starts with the same prefix (blocks shared copy-on-write), the
-// decode above streams the prefix once per row.  This pass reads it once per workgroup and
-// scores it against many rows' queries together, which makes the prefix a dense contraction
-// on MFMA: for KV head g, S = Q_g . K_prefix^T over all B * G query rows of that head.  A
-// workgroup takes one KV head, 128 query columns (8 waves x 16 MFMA columns) and one
-// partition of the prefix.  64-token stages of K and V pass through LDS once for all 8 waves
-// (fp8 is widened to 16 bits on the way in), double-buffered so the next stage's loads fly
-// while the current one is computed.  Each wave runs the online softmax of its 16 columns;
-// QK^T and PV both use v_mfma_f32_16x16x32 (PV takes two 16-token sub-tiles per step).  The
-// result is one (m, l, o) partial per (row, head, prefix partition), merged with the suffix
-// partials by the reduce.
+// Two passes score MANY query columns against one KV head's tokens, which makes them dense
+// contractions on the matrix cores rather than streams:
+//  * the shared-prefix pass: when every row of a batch starts with the same blocks (shared
+//    copy-on-write), the decode above would stream the prefix once per row.  Here it is read
+//    once per workgroup and scored against many rows' queries together: for KV head g,
+//    S = Q_g . K_prefix^T over all B * G query rows of that head;
+//  * multi-query attention with many new tokens per sequence (chunked prefill, long draft
+//    verification): for sequence b and KV head g the G * L (head, new token) pairs are the
+//    columns, each with its own causal limit.
+// Both share one core.  A workgroup of NW waves takes one KV head, a block of NW * CT * 16
+// columns and a token range.  64-token stages of K and V pass through LDS once for all waves
+// (fp8 is widened to 16 bits on the way in), double-buffered, so the next stage's global loads
+// fly while the current one is computed.  Each wave owns CT tiles of 16 columns and runs their
+// online softmax; QK^T and PV both use v_mfma_f32_16x16x32, and each K or V operand read from
+// LDS feeds all CT column tiles of the wave.
 
-constexpr int kPrefixWaves = 8;
-constexpr int kPrefixCols = 16 * kPrefixWaves;   // query columns per workgroup
-constexpr int kPrefixStage = 64;                 // tokens per LDS stage
-
-struct PrefixParams {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  const int32_t* bt;      // the first entries of row 0 are the prefix's blocks
-  const int32_t* lens;
-  float* tmp_out;
-  float* max_logits;
-  float* exp_sums;
-  int B, Hq, Hkv, G, num_blocks, cap;
-  int bs_shift;           // log2(block_size)
-  int prefix_len;         // tokens of the shared prefix, a multiple of 16
-  int chunk;              // tokens per prefix partition, a multiple of 16
-  int parts;              // prefix partitions
-  int hp8;                // Hkv * parts rounded up to a multiple of 8 (the grid's stride)
-  int Pslots;
-  float c2, v_scale;
-};
+constexpr int kStage = 64;                       // tokens per LDS stage
 
 template <int D, int KV>
-struct PrefixTile {
+struct StageGeom {
   static constexpr int ESZ = (KV == KFP8) ? 1 : 2;
   static constexpr int ROWB = D * ESZ;                          // source bytes per (token, head)
   static constexpr int CPRS = ROWB / 16;                        // 16-byte source chunks per row
   static constexpr int CPR = D / 8;                             // 16-byte chunks of a 16-bit row
-  static constexpr int NCH = kPrefixStage * CPRS;               // source chunks per stage and pool
-  static constexpr int NLD = (NCH + 64 * kPrefixWaves - 1) / (64 * kPrefixWaves);
-  static constexpr int KST = kPrefixStage * D * 2;              // one pool's stage in LDS
+  static constexpr int NCH = kStage * CPRS;                     // source chunks per stage and pool
+  static constexpr int KST = kStage * D * 2;                    // one pool's stage in LDS
   static constexpr int SUB = 16 * D * 2;                        // a 16-token sub-tile
   static constexpr int STAGE = 2 * KST;                         // K, then V
   static constexpr int LDS_BYTES = 2 * STAGE;                   // double-buffered: 64 KiB at D = 128
   static constexpr int NS = D / 32;
   static constexpr int NT = D / 16;
+};
+
+// Where a pass's stage rows come from: KV head g of both pools, through one block-table row.
+struct StageSrc {
+  const char* kc;          // K pool, advanced to head g
+  const char* vc;
+  const int32_t* row;      // the block-table row
+  int rowstride;           // bytes between consecutive tokens of a block
+  size_t blockbytes;
+  int bs_shift;            // log2(block_size)
+  int lastcol;             // last entry of the row (indices are clamped to it)
+  unsigned nbm1;           // num_blocks - 1 (ids are clamped to it)
 };
 
 // K rows in LDS: chunk c of row t sits at c ^ swizzle(t), so the 16 rows that one MFMA
@@ -934,222 +956,207 @@ __device__ __forceinline__ int kslot(int t, int c) {
   return t * CPR + (c ^ swz);
 }
 
-template <int D, int KV, bool BF>
-__global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixParams a) {
-  using PT = PrefixTile<D, KV>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int grp = lane >> 4;
-  const int wl = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Workgroup w = hc + hp8 * qb: (KV head, partition) hc, query block qb.  Workgroups are dealt
-  // to the 8 XCDs round-robin by w, so all query blocks of one (head, partition) land on the
-  // same XCD and read its slice of the prefix through one L2.
-  const int hc = blockIdx.x % a.hp8;
-  const int qb = blockIdx.x / a.hp8;
-  if (hc >= a.Hkv * a.parts) return;                          // padding of the stride
-  const int g = hc % a.Hkv;                                   // KV head
-  const int part = hc / a.Hkv;
-  const int c0 = part * a.chunk;                              // the partition: tokens [c0, c1)
-  const int c1 = min(c0 + a.chunk, a.prefix_len);
-  const int nst = (c1 - c0 + kPrefixStage - 1) / kPrefixStage;
-  const int rowstride = a.Hkv * PT::ROWB;
-  const size_t blockbytes = (size_t)rowstride << a.bs_shift;
-  const int bsm1 = (1 << a.bs_shift) - 1;
-  const unsigned nbm1 = (unsigned)(a.num_blocks - 1);
+// The workgroup's stage pipeline: thread tid moves source chunks tid, tid + 64 * NW, ... of K
+// and of V.  Rows at or past `tend` are zero in LDS.  The block ids of a stage's rows are
+// loaded one stage before its K/V rows, so the row loads never wait on them.
+template <int D, int KV, bool BF, int NW>
+struct Stages {
+  using SG = StageGeom<D, KV>;
+  static constexpr int NLD = (SG::NCH + 64 * NW - 1) / (64 * NW);
+  u32x4 kreg[NLD], vreg[NLD];
+  int idn[NLD];
 
-  // ---- stages: thread tid moves source chunks tid, tid + 512, ... of K and of V.  Rows past
-  // the partition's end are zero in LDS.  The block ids of a stage's rows (row 0 of the table)
-  // are loaded one stage before its K/V rows, so the row loads never wait on them.
-  u32x4 kreg[PT::NLD], vreg[PT::NLD];
-  int idn[PT::NLD];
-  auto load_ids = [&](int tok0) {
+  __device__ __forceinline__ void load_ids(const StageSrc& s, int tid, int tok0, int tend) {
 #pragma unroll
-    for (int k = 0; k < PT::NLD; ++k) {
-      const int ci = tid + k * 64 * kPrefixWaves;
-      const int tok = tok0 + ci / PT::CPRS;
-      idn[k] = (ci < PT::NCH && tok < c1) ? a.bt[tok >> a.bs_shift] : 0;
+    for (int k = 0; k < NLD; ++k) {
+      const int ci = tid + k * 64 * NW;
+      const int tok = tok0 + ci / SG::CPRS;
+      idn[k] = (ci < SG::NCH && tok < tend) ? s.row[min(tok >> s.bs_shift, s.lastcol)] : 0;
     }
-  };
-  auto load_stage = [&](int tok0) {
+  }
+  __device__ __forceinline__ void load(const StageSrc& s, int tid, int tok0, int tend) {
+    const int bsm1 = (1 << s.bs_shift) - 1;
 #pragma unroll
-    for (int k = 0; k < PT::NLD; ++k) {
-      const int ci = tid + k * 64 * kPrefixWaves;
-      const int t = ci / PT::CPRS, cs = ci % PT::CPRS;
+    for (int k = 0; k < NLD; ++k) {
+      const int ci = tid + k * 64 * NW;
+      const int t = ci / SG::CPRS, cs = ci % SG::CPRS;
       const int tok = tok0 + t;
       kreg[k] = u32x4{0u, 0u, 0u, 0u};
       vreg[k] = u32x4{0u, 0u, 0u, 0u};
-      if (ci < PT::NCH && tok < c1) {
-        const unsigned id = min((unsigned)idn[k], nbm1);
-        const size_t off = (size_t)id * blockbytes + (size_t)(tok & bsm1) * rowstride +
-                           (size_t)g * PT::ROWB + (size_t)cs * 16;
-        kreg[k] = *(const u32x4*)((const char*)a.kc + off);
-        vreg[k] = *(const u32x4*)((const char*)a.vc + off);
+      if (ci < SG::NCH && tok < tend) {
+        const unsigned id = min((unsigned)idn[k], s.nbm1);
+        const size_t off = (size_t)id * s.blockbytes + (size_t)(tok & bsm1) * s.rowstride + (size_t)cs * 16;
+        kreg[k] = *(const u32x4*)(s.kc + off);
+        vreg[k] = *(const u32x4*)(s.vc + off);
       }
     }
-  };
-  auto store_stage = [&](char* st) {
-#pragma unroll
-    for (int k = 0; k < PT::NLD; ++k) {
-      const int ci = tid + k * 64 * kPrefixWaves;
-      if (ci >= PT::NCH) continue;
-      const int t = ci / PT::CPRS, cs = ci % PT::CPRS;
-      char* vst = st + PT::KST + (t >> 4) * PT::SUB;
-      if constexpr (KV == KFP8) {
-        u32x4 lo, hi;
-        fp8x16_to_16<BF>(kreg[k], lo, hi);
-        *(u32x4*)(st + kslot<PT::CPR>(t, 2 * cs) * 16) = lo;
-        *(u32x4*)(st + kslot<PT::CPR>(t, 2 * cs + 1) * 16) = hi;
-        fp8x16_to_16<BF>(vreg[k], lo, hi);
-        *(u32x4*)(vst + lds_slot<PT::CPR>(t & 15, 2 * cs) * 16) = lo;
-        *(u32x4*)(vst + lds_slot<PT::CPR>(t & 15, 2 * cs + 1) * 16) = hi;
-      } else {
-        *(u32x4*)(st + kslot<PT::CPR>(t, cs) * 16) = kreg[k];
-        *(u32x4*)(vst + lds_slot<PT::CPR>(t & 15, cs) * 16) = vreg[k];
-      }
-    }
-  };
-  load_ids(c0);
-  load_stage(c0);
-  load_ids(c0 + kPrefixStage);
-
-  // ---- this wave's 16 query columns: column c is (sequence c / G, head g * G + c % G).
-  // Column c sees the first min(n, prefix_len) tokens of the prefix; inside this partition,
-  // the tokens below lim (the zero rows past the partition's end are not tokens).
-  const int BG = a.B * a.G;
-  const int cb = qb * kPrefixCols + wl * 16;
-  const bool active = cb < BG;                                // wave-uniform
-  const int col = cb + (lane & 15);
-  const bool cvalid = col < BG;
-  const int cc = cvalid ? col : BG - 1;
-  const int b = cc / a.G;
-  const int head = g * a.G + (cc - b * a.G);
-  const int lim = cvalid ? min(min(clamp_len(a.lens[b], a.cap), a.prefix_len), c1) : 0;
-  // V rows at or past every column's limit are masked: no column of the wave may see them,
-  // and such slots of shared blocks may hold stale bytes
-  int wlim = lim;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) wlim = max(wlim, __shfl_xor(wlim, o));
-  wlim = __builtin_amdgcn_readfirstlane(wlim);
-  u32x4 qv[PT::NS];
-  {
-    const char* qrow = (const char*)a.q + ((size_t)b * a.Hq + head) * D * 2;
-#pragma unroll
-    for (int s = 0; s < PT::NS; ++s) qv[s] = *(const u32x4*)(qrow + (32 * s + 8 * grp) * 2);
   }
-  int koff[PT::NS];
+  __device__ __forceinline__ void store(char* st, int tid) {
 #pragma unroll
-  for (int s = 0; s < PT::NS; ++s) koff[s] = kslot<PT::CPR>(lane & 15, 4 * s + grp) * 16;
-  int troff[PT::NT];
-  {
+    for (int k = 0; k < NLD; ++k) {
+      const int ci = tid + k * 64 * NW;
+      if (ci >= SG::NCH) continue;
+      const int t = ci / SG::CPRS, cs = ci % SG::CPRS;
+      char* vst = st + SG::KST + (t >> 4) * SG::SUB;
+      if constexpr (KV == KFP8) {
+        const bool f = fp8_store_flip(ci);                      // ci and the lane agree modulo 8
+        const int c1 = 2 * cs + (f ? 1 : 0), c2 = 2 * cs + (f ? 0 : 1);
+        fp8x16_store_lds<BF>(kreg[k], f, st + kslot<SG::CPR>(t, c1) * 16, st + kslot<SG::CPR>(t, c2) * 16);
+        fp8x16_store_lds<BF>(vreg[k], f, vst + lds_slot<SG::CPR>(t & 15, c1) * 16,
+                             vst + lds_slot<SG::CPR>(t & 15, c2) * 16);
+      } else {
+        *(u32x4*)(st + kslot<SG::CPR>(t, cs) * 16) = kreg[k];
+        *(u32x4*)(vst + lds_slot<SG::CPR>(t & 15, cs) * 16) = vreg[k];
+      }
+    }
+  }
+};
+
+// One wave's CT tiles of 16 query columns: q operands, per-column limits and the online
+// softmax state.  Lane l holds column l % 16 of every tile; the column sees the tokens below
+// its limit.  O^T and the softmax row sums accumulate on the matrix cores.
+template <int D, bool BF, int CT>
+struct ColTiles {
+  static constexpr int NS = D / 32, NT = D / 16, KST = kStage * D * 2, SUB = 16 * D * 2, CPR = D / 8;
+  u32x4 qv[CT][NS];
+  f32x4 acc[CT][NT];
+  f32x4 accL[CT];      // every element: the column's running sum of probabilities
+  float m[CT];         // running maximum (exp2 domain); -inf until the column sees a token
+  int lim[CT];         // this lane's column limit, per tile
+  int wmin, wlim;      // lowest / highest limit over the wave's columns (wave-uniform)
+  int koff[NS], troff[NT];
+  int grp;
+
+  __device__ __forceinline__ void init(int lane) {
+    grp = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = kslot<CPR>(lane & 15, 4 * s + grp) * 16;
     const int tt = 4 * grp + ((lane >> 2) & 3);
     const int qq = lane & 3;
 #pragma unroll
-    for (int T = 0; T < PT::NT; ++T)
-      troff[T] = lds_slot<PT::CPR>(tt, 2 * T + (qq >> 1)) * 16 + (qq & 1) * 8;
+    for (int T = 0; T < NT; ++T) troff[T] = lds_slot<CPR>(tt, 2 * T + (qq >> 1)) * 16 + (qq & 1) * 8;
   }
-  f32x4 acc[PT::NT];
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-  for (int T = 0; T < PT::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-
-  // P^T row sums (the softmax denominators) come from the matrix cores: an A operand of
-  // bf16/f16 ones against the same P^T tile adds sum_t p to every row of accL, so the running
-  // sum is rescaled with the output and needs no cross-lane reduction.
-  const unsigned one2 = BF ? 0x3f803f80u : 0x3c003c00u;
-  const u32x4 ones = {one2, one2, one2, one2};
-  f32x4 accL = {0.f, 0.f, 0.f, 0.f};
-  // Columns of the wave that see every token of a stage need no masks: the lowest limit.
-  int wmin = lim;
+    for (int c = 0; c < CT; ++c) {
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) wmin = min(wmin, __shfl_xor(wmin, o));
-  wmin = __builtin_amdgcn_readfirstlane(wmin);
+      for (int T = 0; T < NT; ++T) acc[c][T] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accL[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[c] = -INFINITY;
+    }
+  }
+  // q row of tile c (d order matching the K operand reads).
+  __device__ __forceinline__ void load_q(int c, const char* qrow) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qv[c][s] = *(const u32x4*)(qrow + (32 * s + 8 * grp) * 2);
+  }
+  // After setting lim[]: the wave's lowest and highest limits.
+  __device__ __forceinline__ void limits_done() {
+    int lo = lim[0], hi = lim[0];
+#pragma unroll
+    for (int c = 1; c < CT; ++c) {
+      lo = min(lo, lim[c]);
+      hi = max(hi, lim[c]);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    wmin = __builtin_amdgcn_readfirstlane(lo);
+    wlim = __builtin_amdgcn_readfirstlane(hi);
+  }
 
-  // One stage for the wave's columns: S^T of four 16-token sub-tiles, one softmax update over
-  // all 64 tokens, then O^T += V^T . P^T two sub-tiles at a time.  MASKED: some column of the
-  // wave stops inside the stage (per-column select on the scores, zeroed V rows past every
-  // column's limit); otherwise the exponent is one fma per score.
-  auto compute = [&](const char* st, int tok0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // One stage for the wave's columns: S^T of four 16-token sub-tiles per column tile, one
+  // softmax update over all 64 tokens, then O^T += V^T . P^T two sub-tiles at a time.  MASKED:
+  // some column of the wave stops inside the stage (per-column select on the scores, zeroed V
+  // rows past every column's limit); otherwise the exponent is one fma per score.
+  template <bool MASKED>
+  __device__ __forceinline__ void compute(const char* st, int tok0, float c2) {
     // Every LDS operand of the stage's QK^T, and the V operands of the first PV half, is
     // requested before the first MFMA; the second half's V reads go out before the softmax.
     // LDS reads of a wave return in order, so each MFMA waits only for its own operand and
     // the LDS latency is paid about once per stage instead of once per MFMA.
-    const char* vst = st + PT::KST;
+    const char* vst = st + KST;
     auto vread = [&](int sub, int T) {
       return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)((lds_char*)(vst + sub * PT::SUB) + troff[T])));
+          (lds_s16x4*)((lds_char*)(vst + sub * SUB) + troff[T])));
     };
-    u32x4 kf[4][PT::NS];
+    u32x4 kf[4][NS];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int s = 0; s < PT::NS; ++s) kf[u][s] = *(const u32x4*)(st + u * PT::SUB + koff[s]);
-    u32x2 vlo[2][PT::NT], vhi[2][PT::NT];
+      for (int s = 0; s < NS; ++s) kf[u][s] = *(const u32x4*)(st + u * SUB + koff[s]);
+    u32x2 vlo[2][NT], vhi[2][NT];
 #pragma unroll
-    for (int T = 0; T < PT::NT; ++T) {
+    for (int T = 0; T < NT; ++T) {
       vlo[0][T] = vread(0, T);
       vhi[0][T] = vread(1, T);
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 sc[4];
+    f32x4 sc[CT][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int s = 0; s < PT::NS; ++s) sc[u] = mfma_16x16x32<BF>(kf[u][s], qv[s], sc[u]);
-    }
+      for (int c = 0; c < CT; ++c) {
+        sc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int T = 0; T < PT::NT; ++T) {
+        for (int s = 0; s < NS; ++s) sc[c][u] = mfma_16x16x32<BF>(kf[u][s], qv[c][s], sc[c][u]);
+      }
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
       vlo[1][T] = vread(2, T);
       vhi[1][T] = vread(3, T);
     }
     __builtin_amdgcn_sched_barrier(0);
-    float x[4][4];
-    float mx;
-    if constexpr (MASKED) {
-      mx = -INFINITY;
+    u32x2 pop[CT][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[u][e] = (tok0 + 16 * u + 4 * grp + e < lim) ? sc[u][e] * a.c2 : -INFINITY;
-          mx = fmaxf(mx, x[u][e]);
-        }
-    } else {
-      // max of c2 * s over the stage = c2 * (max s, or min s for a negative scale)
-      float r = sc[0][0];
-      if (a.c2 >= 0.f) {
+    for (int c = 0; c < CT; ++c) {
+      float x[4][4];
+      float mx;
+      if constexpr (MASKED) {
+        mx = -INFINITY;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r = fmaxf(r, sc[u][e]);
+          for (int e = 0; e < 4; ++e) {
+            x[u][e] = (tok0 + 16 * u + 4 * grp + e < lim[c]) ? sc[c][u][e] * c2 : -INFINITY;
+            mx = fmaxf(mx, x[u][e]);
+          }
       } else {
+        // max of c2 * s over the stage = c2 * (max s, or min s for a negative scale)
+        float r = sc[c][0][0];
+        if (c2 >= 0.f) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r = fminf(r, sc[u][e]);
+            for (int e = 0; e < 4; ++e) r = fmaxf(r, sc[c][u][e]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r = fminf(r, sc[c][u][e]);
+        }
+        mx = r * c2;
       }
-      mx = r * a.c2;
-    }
-    mx = max_rows32(max_rows16(mx));
-    if (__ballot(mx > m) != 0) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-      accL *= alpha;
+      mx = max_rows32(max_rows16(mx));
+      if (__ballot(mx > m[c]) != 0) {
+        const float mn = fmaxf(m[c], mx);
+        const float alpha = m[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - mn);
+        m[c] = mn;
+        accL[c] *= alpha;
 #pragma unroll
-      for (int T = 0; T < PT::NT; ++T) acc[T] *= alpha;
-    }
-    const float mb = m == -INFINITY ? 0.f : m;
-    u32x2 pop[4];
+        for (int T = 0; T < NT; ++T) acc[c][T] *= alpha;
+      }
+      const float mb = m[c] == -INFINITY ? 0.f : m[c];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float pr[4];
+      for (int u = 0; u < 4; ++u) {
+        float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pr[e] = __builtin_amdgcn_exp2f(MASKED ? x[u][e] - mb : __builtin_fmaf(sc[u][e], a.c2, -mb));
-      pop[u] = u32x2{pack2_16<BF>(pr[0], pr[1]), pack2_16<BF>(pr[2], pr[3])};
+        for (int e = 0; e < 4; ++e)
+          pr[e] = __builtin_amdgcn_exp2f(MASKED ? x[u][e] - mb : __builtin_fmaf(sc[c][u][e], c2, -mb));
+        pop[c][u] = u32x2{pack2_16<BF>(pr[0], pr[1]), pack2_16<BF>(pr[2], pr[3])};
+      }
     }
     u32x2 vm[4];
 #pragma unroll
@@ -1163,12 +1170,21 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
         }
       }
     }
+    // P^T row sums (the softmax denominators) come from the matrix cores: an A operand of
+    // bf16/f16 ones against the same P^T tile adds sum_t p to every row of accL, so the running
+    // sum is rescaled with the output and needs no cross-lane reduction.
+    const unsigned one2 = BF ? 0x3f803f80u : 0x3c003c00u;
+    const u32x4 ones = {one2, one2, one2, one2};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4 pb = {pop[2 * h].x, pop[2 * h].y, pop[2 * h + 1].x, pop[2 * h + 1].y};
-      accL = mfma_16x16x32<BF>(ones, pb, accL);
+      u32x4 pb[CT];
 #pragma unroll
-      for (int T = 0; T < PT::NT; ++T) {
+      for (int c = 0; c < CT; ++c) {
+        pb[c] = u32x4{pop[c][2 * h].x, pop[c][2 * h].y, pop[c][2 * h + 1].x, pop[c][2 * h + 1].y};
+        accL[c] = mfma_16x16x32<BF>(ones, pb[c], accL[c]);
+      }
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
         const u32x2 lo = vlo[h][T];
         const u32x2 hi = vhi[h][T];
         u32x4 va;
@@ -1176,38 +1192,42 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
           va = u32x4{lo.x & vm[2 * h].x, lo.y & vm[2 * h].y, hi.x & vm[2 * h + 1].x, hi.y & vm[2 * h + 1].y};
         else
           va = u32x4{lo.x, lo.y, hi.x, hi.y};
-        acc[T] = mfma_16x16x32<BF>(va, pb, acc[T]);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[c][T] = mfma_16x16x32<BF>(va, pb[c], acc[c][T]);
       }
     }
-  };
+  }
 
-  store_stage(smem);
-  // q must be resident before the loop: loads retire in order, so a q load still counted as
-  // outstanding inside the loop would make the first MFMA wait for the next stage's prefetch.
-#pragma unroll
-  for (int s = 0; s < PT::NS; ++s) asm volatile("" : : "v"(qv[s]));
-  __syncthreads();
-  // Stage s: prefetch stage s + 1 into registers, compute stage s from LDS buffer s & 1, store
-  // stage s + 1 into the other buffer, one barrier.  Every wave passes the same barriers.
+  // Column tile c: normalised output (or partial) row of this lane's column, d = 16 T + 4 grp ..
+  __device__ __forceinline__ float denom(int c) const { return accL[c][0]; }
+};
+
+// Runs the stages [t_lo, tend) of one token range for every wave of the workgroup: prefetch
+// stage s + 1 into registers, compute stage s from LDS buffer s & 1, store stage s + 1 into the
+// other buffer, one barrier.  Every wave passes the same barriers (the same number of stages);
+// the stages every column of a wave sees whole come first and take the unmasked compute.
+// Expects stage 0 in LDS buffer 0 and the ids of stage 1 loaded (stage_prologue).
+template <int D, int KV, bool BF, int NW, int CT>
+__device__ __forceinline__ void run_stages(Stages<D, KV, BF, NW>& stg, ColTiles<D, BF, CT>& cols, const StageSrc& src,
+                                           char* smem, int tid, int t_lo, int tend, bool active, float c2) {
+  using SG = StageGeom<D, KV>;
+  const int nst = (tend - t_lo + kStage - 1) / kStage;
   auto stage = [&](int s, char* cur, char* nxt, auto masked_tag) {
     const bool more = s + 1 < nst;                              // uniform over the workgroup
     if (more) {
-      load_stage(c0 + (s + 1) * kPrefixStage);
-      load_ids(c0 + (s + 2) * kPrefixStage);
+      stg.load(src, tid, t_lo + (s + 1) * kStage, tend);
+      stg.load_ids(src, tid, t_lo + (s + 2) * kStage, tend);
     }
-    if (active) compute(cur, c0 + s * kPrefixStage, masked_tag);
-    if (more) store_stage(nxt);
+    if (active) cols.template compute<decltype(masked_tag)::value>(cur, t_lo + s * kStage, c2);
+    if (more) stg.store(nxt, tid);
     __syncthreads();
   };
-  // The stages every column of this wave sees whole come first and need no masks; they run
-  // unrolled by two so the LDS buffer offsets are immediates.  The rest (usually the last
-  // stage or none) runs the masked compute.  Keeping the two apart also keeps the
-  // accumulators in place instead of merging two paths every stage.
-  int nfast = active ? (wmin - c0) / kPrefixStage : 0;
+  int nfast = active ? (cols.wmin - t_lo) / kStage : 0;
   nfast = nfast < 0 ? 0 : (nfast > nst ? nst : nfast);
   char* const buf0 = smem;
-  char* const buf1 = smem + PT::STAGE;
+  char* const buf1 = smem + SG::STAGE;
   int s = 0;
+  // unrolled by two so the LDS buffer offsets are immediates
   for (; s + 2 <= nfast; s += 2) {
     stage(s, buf0, buf1, std::false_type{});
     stage(s + 1, buf1, buf0, std::false_type{});
@@ -1217,19 +1237,258 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void pa_prefix_kernel(PrefixPara
     ++s;
   }
   for (; s < nst; ++s) stage(s, (s & 1) ? buf1 : buf0, (s & 1) ? buf0 : buf1, std::true_type{});
+}
+
+// Stage 0 of [t_lo, tend) into LDS buffer 0, the ids of stage 1 loaded, one barrier.
+template <int D, int KV, bool BF, int NW>
+__device__ __forceinline__ void stage_prologue(Stages<D, KV, BF, NW>& stg, const StageSrc& src, char* smem, int tid,
+                                               int t_lo, int tend) {
+  stg.load_ids(src, tid, t_lo, tend);
+  stg.load(src, tid, t_lo, tend);
+  stg.load_ids(src, tid, t_lo + kStage, tend);
+  stg.store(smem, tid);
+  __syncthreads();
+}
+
+// ---- the shared-prefix pass
+// Configuration: eight waves of one 16-column tile (128 query columns per workgroup), two waves
+// per SIMD; four waves of two tiles (one wave per SIMD, half the LDS reads per column) measured
+// slower.
+constexpr int kPrefixWaves = 8;
+constexpr int kPrefixCT = 1;
+constexpr int kPrefixCols = 16 * kPrefixCT * kPrefixWaves;   // query columns per workgroup
+
+struct PrefixParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;      // the first entries of row 0 are the prefix's blocks
+  const int32_t* lens;
+  float* tmp_out;
+  float* max_logits;
+  float* exp_sums;
+  int B, Hq, Hkv, G, num_blocks, cap, max_blocks;
+  int bs_shift;           // log2(block_size)
+  int prefix_len;         // tokens of the shared prefix, a multiple of 16
+  int chunk;              // tokens per prefix partition, a multiple of 16
+  int parts;              // prefix partitions
+  int hp8;                // Hkv * parts rounded up to a multiple of 8 (the grid's stride)
+  int Pslots;
+  float c2, v_scale;
+};
+
+// One workgroup per (KV head, prefix partition, block of query columns); column c of the batch
+// is (sequence c / G, head g * G + c % G) and sees the first min(n, prefix_len) tokens.  The
+// result is one (m, l, o) partial per (row, head, prefix partition), merged with the suffix
+// partials by the reduce.
+// One tile per wave fits two waves per SIMD; two tiles per wave take the whole register file.
+template <int D, int KV, bool BF, int NW, int CT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 2 : 1)))
+void pa_prefix_kernel(PrefixParams a) {
+  constexpr int COLS = 16 * CT * NW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wl = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroup w = hc + hp8 * qb: (KV head, partition) hc, query block qb.  Workgroups are dealt
+  // to the 8 XCDs round-robin by w, so all query blocks of one (head, partition) land on the
+  // same XCD and read its slice of the prefix through one L2.
+  const int hc = blockIdx.x % a.hp8;
+  const int qb = blockIdx.x / a.hp8;
+  if (hc >= a.Hkv * a.parts) return;                          // padding of the stride
+  const int g = hc % a.Hkv;                                   // KV head
+  const int part = hc / a.Hkv;
+  const int c0 = part * a.chunk;                              // the partition: tokens [c0, c1)
+  const int c1 = min(c0 + a.chunk, a.prefix_len);
+  StageSrc src;
+  src.rowstride = a.Hkv * StageGeom<D, KV>::ROWB;
+  src.kc = (const char*)a.kc + (size_t)g * StageGeom<D, KV>::ROWB;
+  src.vc = (const char*)a.vc + (size_t)g * StageGeom<D, KV>::ROWB;
+  src.row = a.bt;
+  src.blockbytes = (size_t)src.rowstride << a.bs_shift;
+  src.bs_shift = a.bs_shift;
+  src.lastcol = a.max_blocks - 1;
+  src.nbm1 = (unsigned)(a.num_blocks - 1);
+
+  Stages<D, KV, BF, NW> stg;
+  stg.load_ids(src, tid, c0, c1);
+  stg.load(src, tid, c0, c1);
+  stg.load_ids(src, tid, c0 + kStage, c1);
+
+  // ---- this wave's columns (V rows at or past every column's limit are masked: such slots of
+  // shared blocks may hold stale bytes)
+  const int BG = a.B * a.G;
+  const int cb = qb * COLS + wl * 16 * CT;
+  const bool active = cb < BG;                                // wave-uniform
+  ColTiles<D, BF, CT> cols;
+  cols.init(lane);
+  cols.reset();
+  int bcol[CT], hcol[CT];
+  bool cvalid[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int col = cb + 16 * c + (lane & 15);
+    cvalid[c] = col < BG;
+    const int cc = cvalid[c] ? col : BG - 1;
+    bcol[c] = cc / a.G;
+    hcol[c] = g * a.G + (cc - bcol[c] * a.G);
+    cols.lim[c] = cvalid[c] ? min(min(clamp_len(a.lens[bcol[c]], a.cap), a.prefix_len), c1) : 0;
+    cols.load_q(c, (const char*)a.q + ((size_t)bcol[c] * a.Hq + hcol[c]) * D * 2);
+  }
+  cols.limits_done();
+  stg.store(smem, tid);
+  // q must be resident before the loop: loads retire in order, so a q load still counted as
+  // outstanding inside the loop would make the first MFMA wait for the next stage's prefetch.
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int s = 0; s < StageGeom<D, KV>::NS; ++s) asm volatile("" : : "v"(cols.qv[c][s]));
+  __syncthreads();
+  run_stages(stg, cols, src, smem, tid, c0, c1, active, a.c2);
 
   if (!active) return;
-  const float l = accL[0];
-  const float inv = l > 0.f ? a.v_scale / l : 0.f;
-  if (cvalid) {
-    const size_t prow = ((size_t)b * a.Hq + head) * a.Pslots + part;
-    float* orow = a.tmp_out + prow * D;
 #pragma unroll
-    for (int T = 0; T < PT::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
-    if (grp == 0) {
-      a.max_logits[prow] = m * kLn2;
-      a.exp_sums[prow] = l;
+  for (int c = 0; c < CT; ++c) {
+    const float l = cols.denom(c);
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    if (cvalid[c]) {
+      const size_t prow = ((size_t)bcol[c] * a.Hq + hcol[c]) * a.Pslots + part;
+      float* orow = a.tmp_out + prow * D;
+#pragma unroll
+      for (int T = 0; T < StageGeom<D, KV>::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * cols.grp) = cols.acc[c][T] * inv;
+      if (cols.grp == 0) {
+        a.max_logits[prow] = cols.m[c] * kLn2;
+        a.exp_sums[prow] = l;
+      }
     }
+  }
+}
+
+// ---- multi-query attention with many new tokens per sequence
+// A workgroup of NW waves of CT 16-column tiles serves one KV head, one block of NW * CT * 16
+// (head, new token) columns and the token ranges of its schedule.
+
+// grid.y = g * col_blocks + column block.  Column c of a sequence's block is (query head
+// g * G + c / L, new token i = c % L); token i sits at position n - L + i and sees the first
+// n - (L - 1 - i) tokens.  Modes: one workgroup per sequence (final rows), per fixed partition
+// or per range of the balanced split (partials for paged_attn_reduce over L * Hq rows).
+template <int D, int KV, bool BF, int MODE, int NW, int CT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 2 : 1)))
+void pa_mq_tiled_kernel(DecodeParams a, int col_blocks) {
+  constexpr int COLS = 16 * CT * NW;
+  using SG = StageGeom<D, KV>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wl = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.y / col_blocks;
+  const int cbk = blockIdx.y - g * col_blocks;
+  const int GL = a.G * a.L;
+  const int cb = cbk * COLS + wl * 16 * CT;                   // the wave's first column
+  const bool active = cb < GL;                                // wave-uniform
+  const int cap = a.cap;
+
+  SegSource segs;
+  segs.mode = MODE;
+  segs.w = 0;
+  Seg cur;
+  if constexpr (MODE == MODE_SINGLE) {
+    cur.b = blockIdx.x;
+    cur.n = clamp_len(__builtin_amdgcn_readfirstlane(a.lens[cur.b]), cap);
+    cur.tlo = 0;
+    cur.thi = (cur.n + 15) >> 4;
+    cur.slot = -1;
+    cur.valid = true;
+  } else if constexpr (MODE == MODE_FIXED) {
+    cur.b = blockIdx.z;
+    cur.n = clamp_len(__builtin_amdgcn_readfirstlane(a.lens[cur.b]), cap);
+    cur.slot = blockIdx.x;
+    cur.tlo = (cur.slot * a.PS) >> 4;
+    cur.thi = (min((cur.slot + 1) * a.PS, cur.n) + 15) >> 4;
+    cur.valid = cur.thi > cur.tlo;
+    if (!cur.valid) return;
+  } else {
+    if (!balanced_start(segs, cur, a.lens, a.B, cap, 0, a.W, blockIdx.x, lane)) return;
+  }
+
+  StageSrc src;
+  src.rowstride = a.Hkv * SG::ROWB;
+  src.kc = (const char*)a.kc + (size_t)g * SG::ROWB;
+  src.vc = (const char*)a.vc + (size_t)g * SG::ROWB;
+  src.blockbytes = (size_t)src.rowstride * a.BS;
+  src.bs_shift = a.tile_shift + 4;
+  src.lastcol = a.max_blocks - 1;
+  src.nbm1 = (unsigned)(a.num_blocks - 1);
+
+  Stages<D, KV, BF, NW> stg;
+  ColTiles<D, BF, CT> cols;
+  cols.init(lane);
+  int hcol[CT], icol[CT];
+  bool cvalid[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int col = cb + 16 * c + (lane & 15);
+    cvalid[c] = col < GL;
+    const int cc = cvalid[c] ? col : 0;
+    hcol[c] = g * a.G + cc / a.L;
+    icol[c] = cc % a.L;
+  }
+
+  for (;;) {
+    // ---- one segment: tokens [t_lo, tend) of sequence cur.b
+    const int t_lo = cur.tlo << 4;
+    const int tend = min(cur.thi << 4, cur.n);
+    src.row = a.bt + (size_t)cur.b * a.max_blocks;
+    stg.load_ids(src, tid, t_lo, tend);
+    stg.load(src, tid, t_lo, tend);
+    stg.load_ids(src, tid, t_lo + kStage, tend);
+    cols.reset();
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      cols.lim[c] = cvalid[c] ? min(cur.n - (a.L - 1 - icol[c]), tend) : 0;
+      cols.load_q(c, (const char*)a.q + (((size_t)cur.b * a.L + icol[c]) * a.Hq + hcol[c]) * D * 2);
+    }
+    cols.limits_done();
+    stg.store(smem, tid);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int s = 0; s < SG::NS; ++s) asm volatile("" : : "v"(cols.qv[c][s]));
+    __syncthreads();
+    run_stages(stg, cols, src, smem, tid, t_lo, tend, active, a.c2);
+
+    // ---- the segment's rows: final output (single pass) or a partial
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        if (!cvalid[c]) continue;
+        const float l = cols.denom(c);
+        const float inv = l > 0.f ? a.v_scale / l : 0.f;
+        const size_t row = ((size_t)cur.b * a.L + icol[c]) * a.Hq + hcol[c];
+        if constexpr (MODE == MODE_SINGLE) {
+          unsigned short* orow = (unsigned short*)a.out + row * D;
+#pragma unroll
+          for (int T = 0; T < SG::NT; ++T) {
+            u32x2 wv;
+            wv.x = pack2_16<BF>(cols.acc[c][T][0] * inv, cols.acc[c][T][1] * inv);
+            wv.y = pack2_16<BF>(cols.acc[c][T][2] * inv, cols.acc[c][T][3] * inv);
+            *(u32x2*)(orow + 16 * T + 4 * cols.grp) = wv;
+          }
+        } else if (cur.slot >= 0 && cur.slot < a.Pslots) {
+          const size_t prow = row * a.Pslots + cur.slot;
+          float* orow = a.tmp_out + prow * D;
+#pragma unroll
+          for (int T = 0; T < SG::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * cols.grp) = cols.acc[c][T] * inv;
+          if (cols.grp == 0) {
+            a.max_logits[prow] = cols.m[c] * kLn2;
+            a.exp_sums[prow] = l;
+          }
+        }
+      }
+    }
+    if constexpr (MODE != MODE_BALANCED) break;
+    cur = segs.next(cur, lane);
+    if (!cur.valid) break;
   }
 }
 
@@ -1443,6 +1702,9 @@ void launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, bool la
     hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
 
+// New query tokens per sequence accepted by paged_attn_multi_query.
+constexpr int kMaxQueryLen = 4096;
+
 // Partial slots per (sequence, head): fixed partitions need ceil(max_len / PS); a balanced
 // split gives every workgroup >= kMinChunkTiles units, and a sequence's tiles are consecutive
 // units, so a sequence meets at most ceil(tiles / kMinChunkTiles) + 1 ranges.
@@ -1472,6 +1734,43 @@ void launch_decode_policy(const DecodeParams& p, bool last, hipStream_t st) {
     launch(pa_decode_kernel<D, KV, BF, MODE_BALANCED, POLICY>, dim3(p.W, HG), dim3(64 * nw), lds, st, last, p);
 }
 
+// Multi-query with more (head, new token) columns than one MFMA tile holds: the tiled kernel,
+// one workgroup per (work item, KV head, block of kMqCols columns).  Eight waves of one
+// 16-column tile, two waves per SIMD: measured faster than four waves (one per SIMD) of two
+// tiles each, and than four-wave workgroups of one tile, at every q_len tried.
+constexpr int kMqWaves = 8, kMqCT = 1;
+constexpr int kMqCols = 16 * kMqWaves * kMqCT;
+int mq_col_blocks(int G, int L) { return (G * L + kMqCols - 1) / kMqCols; }
+
+template <int D, int KV, bool BF, int NW, int CT>
+void launch_mq_tiled_cfg(const DecodeParams& p, bool last, hipStream_t st) {
+  const int CB = mq_col_blocks(p.G, p.L);
+  const unsigned gy = (unsigned)(p.Hkv * CB);
+  const size_t lds = (size_t)StageGeom<D, KV>::LDS_BYTES;
+  const dim3 block(64 * NW);
+  if (p.mode == MODE_SINGLE)
+    launch(pa_mq_tiled_kernel<D, KV, BF, MODE_SINGLE, NW, CT>, dim3(p.B, gy), block, lds, st, last, p, CB);
+  else if (p.mode == MODE_FIXED)
+    launch(pa_mq_tiled_kernel<D, KV, BF, MODE_FIXED, NW, CT>, dim3(p.Pslots, gy, p.B), block, lds, st, last, p, CB);
+  else
+    launch(pa_mq_tiled_kernel<D, KV, BF, MODE_BALANCED, NW, CT>, dim3(p.W, gy), block, lds, st, last, p, CB);
+}
+
+// Tiled multi-query workgroups resident per compute unit (balanced schedule) for this shape.
+template <int D, int KV, bool BF>
+int mq_occupancy() {
+  int nb = 0;
+  const size_t lds = (size_t)StageGeom<D, KV>::LDS_BYTES;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &nb, (const void*)pa_mq_tiled_kernel<D, KV, BF, MODE_BALANCED, kMqWaves, kMqCT>, 64 * kMqWaves, lds);
+  return e == hipSuccess && nb > 0 ? nb : 1;
+}
+
+template <int D, int KV, bool BF>
+void launch_mq_tiled(const DecodeParams& p, bool last, hipStream_t st) {
+  launch_mq_tiled_cfg<D, KV, BF, kMqWaves, kMqCT>(p, last, st);
+}
+
 // The balanced decode with the step's new rows appended in the same launch (16-bit caches).
 template <int D, int KV, bool BF>
 void launch_decode_append(const DecodeParams& p, bool shared_blocks, hipStream_t st) {
@@ -1498,8 +1797,8 @@ template <int D, int KV, bool BF>
 void launch_prefix(const PrefixParams& p, hipStream_t st) {
   const long long qblocks = ((long long)p.B * p.G + kPrefixCols - 1) / kPrefixCols;
   const dim3 grid((unsigned)(qblocks * p.hp8));
-  const size_t lds = (size_t)PrefixTile<D, KV>::LDS_BYTES;
-  launch(pa_prefix_kernel<D, KV, BF>, grid, dim3(64 * kPrefixWaves), lds, st, false, p);
+  const size_t lds = (size_t)StageGeom<D, KV>::LDS_BYTES;
+  launch(pa_prefix_kernel<D, KV, BF, kPrefixWaves, kPrefixCT>, grid, dim3(64 * kPrefixWaves), lds, st, false, p);
 }
 
 void launch_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
@@ -1679,11 +1978,11 @@ static int check_attn(void* out, const void* query, const void* key_cache, const
                       float k_scale, float v_scale, int max_context_len, int partition_size,
                       float* tmp_out, float* max_logits, float* exp_sums, int flags) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks < 0 || num_blocks < 0 ||
-      max_context_len < 0 || partition_size < -(1 << 20) || q_len < 1 || q_len > 16)
+      max_context_len < 0 || partition_size < -(1 << 20) || q_len < 1 || q_len > kMaxQueryLen)
     return PKV_ERR_SHAPE;
   if ((flags & ~PKV_FLAG_SHARED_BLOCKS) != 0) return PKV_ERR_SHAPE;
-  if (num_heads % num_kv_heads != 0 || (num_heads / num_kv_heads) * q_len > 16 || num_kv_heads > 16)
-    return PKV_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16 || num_kv_heads > 16) return PKV_ERR_SHAPE;
+  if ((long long)num_kv_heads * mq_col_blocks(num_heads / num_kv_heads, q_len) > 65535) return PKV_ERR_SHAPE;
   if ((long long)num_seqs * q_len * num_heads >= (1LL << 31)) return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_SHAPE;
   if (block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0) return PKV_ERR_SHAPE;
@@ -1780,6 +2079,16 @@ static void launch_decode_dt(const DecodeParams& p, int head_dim, int q_dtype, i
                              hipStream_t st) {
   const bool bf = q_dtype == PKV_BF16;
   const bool f8 = kv_dtype == PKV_FP8_E4M3;
+  if (p.G * p.L > 16) {                                     // more columns than one MFMA tile
+    if (head_dim == 128) {
+      if (f8) { if (bf) launch_mq_tiled<128, KFP8, true>(p, last, st); else launch_mq_tiled<128, KFP8, false>(p, last, st); }
+      else    { if (bf) launch_mq_tiled<128, KBF16, true>(p, last, st); else launch_mq_tiled<128, KF16, false>(p, last, st); }
+    } else {
+      if (f8) { if (bf) launch_mq_tiled<64, KFP8, true>(p, last, st); else launch_mq_tiled<64, KFP8, false>(p, last, st); }
+      else    { if (bf) launch_mq_tiled<64, KBF16, true>(p, last, st); else launch_mq_tiled<64, KF16, false>(p, last, st); }
+    }
+    return;
+  }
   if (head_dim == 128) {
     if (f8) { if (bf) launch_decode<128, KFP8, true>(p, sh, last, st); else launch_decode<128, KFP8, false>(p, sh, last, st); }
     else    { if (bf) launch_decode<128, KBF16, true>(p, sh, last, st); else launch_decode<128, KF16, false>(p, sh, last, st); }
@@ -1990,6 +2299,7 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
     pp.G = num_heads / num_kv_heads;
     pp.num_blocks = num_blocks;
     pp.cap = p.cap;
+    pp.max_blocks = max_blocks;
     pp.bs_shift = __builtin_ctz((unsigned)block_size);
     pp.prefix_len = prefix_len;
     pp.chunk = prefix_partition_size;
@@ -2021,6 +2331,30 @@ int paged_attn_shared_prefix_slots(int max_context_len, int prefix_len, int pref
   return shared_prefix_slots(max_context_len, prefix_len, prefix_partition_size, partition_size);
 }
 
+int paged_attn_multi_query_split(int num_heads, int num_kv_heads, int head_dim, int q_len, int q_dtype,
+                                 int kv_dtype) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > 16 || num_heads % num_kv_heads != 0 || q_len < 1 ||
+      q_len > kMaxQueryLen || (head_dim != 64 && head_dim != 128))
+    return 0;
+  const int G = num_heads / num_kv_heads;
+  if (G * q_len <= 16) return paged_attn_balanced_split(num_kv_heads, head_dim, q_dtype, kv_dtype);
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  // fill every compute unit once: W ranges x Hkv heads x column blocks tiled workgroups
+  const bool bf = q_dtype == PKV_BF16, f8 = kv_dtype == PKV_FP8_E4M3;
+  int occ;
+  if (head_dim == 128)
+    occ = f8 ? (bf ? mq_occupancy<128, KFP8, true>() : mq_occupancy<128, KFP8, false>())
+             : (bf ? mq_occupancy<128, KBF16, true>() : mq_occupancy<128, KF16, false>());
+  else
+    occ = f8 ? (bf ? mq_occupancy<64, KFP8, true>() : mq_occupancy<64, KFP8, false>())
+             : (bf ? mq_occupancy<64, KBF16, true>() : mq_occupancy<64, KF16, false>());
+  const long long per_w = (long long)num_kv_heads * mq_col_blocks(G, q_len);
+  const long long w = (long long)prop.multiProcessorCount * occ / per_w;
+  return -(int)(w > 0 ? w : 1);
+}
+
 int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int prefix_len) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || prefix_len <= 0)
     return 0;
@@ -2032,7 +2366,7 @@ int paged_attn_prefix_split(int num_seqs, int num_heads, int num_kv_heads, int p
   long long parts = (prop.multiProcessorCount + units - 1) / units;
   if (parts < 1) parts = 1;
   long long size = (prefix_len + parts - 1) / parts;
-  size = (size + kPrefixStage - 1) / kPrefixStage * kPrefixStage;
+  size = (size + kStage - 1) / kStage * kStage;
   return (int)size;
 }
 

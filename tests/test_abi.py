@@ -36,6 +36,7 @@ def test_library_exports_every_declared_symbol():
                           "paged_kv_swap_blocks", "pkv_bm_create", "pkv_bm_append", "pkv_bm_check",
                           "paged_attn_workspace_bytes", "paged_attn_partial_slots",
                           "paged_attn_balanced_split", "pkv_status_string", "paged_attn_decode_noalloc",
+                          "paged_attn_multi_query_split",
                           "pkv_time_next_call"}
     L = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -108,8 +109,8 @@ def _mq(**kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(L=0), E_SHAPE),
-    (dict(L=5), E_SHAPE),                      # G = 4 query heads x 5 tokens > 16 MFMA columns
-    (dict(Hq=16, Hkv=1, L=2), E_SHAPE),        # 16 x 2 > 16
+    (dict(L=4097), E_SHAPE),                   # more new tokens than the supported 4096
+    (dict(Hq=34, Hkv=2, L=2), E_SHAPE),        # a group of 17 query heads
     (dict(PS=-64), E_WS),
     (dict(out=None), E_NULL),
 ])
@@ -389,3 +390,10 @@ def test_noalloc_rejects(kw, want):
 
 def test_noalloc_zero_sequences_is_a_noop():
     assert _noalloc(B=0, q=None, out=None) == OK
+
+
+def test_multi_query_split_without_device_or_bad_shape():
+    L = pk.lib()
+    assert L.paged_attn_multi_query_split(32, 8, 96, 16, 1, 1) == 0        # head_dim 96
+    assert L.paged_attn_multi_query_split(32, 8, 128, 0, 1, 1) == 0        # q_len 0
+    assert L.paged_attn_multi_query_split(34, 2, 128, 2, 1, 1) == 0        # group of 17
