@@ -145,29 +145,43 @@ SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA",
                "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]
 
 
-def sq_commands(workload: str, schedule: str, out: str = "OUT") -> list:
+OUR_KERNELS = ("pa_decode", "pa_prefix", "pa_reduce", "kv_write", "pa_mq_tiled")
+
+
+def _bench_args(workload: str, schedule: str, bench_args: str = "") -> str:
+    return bench_args or f"--workload {workload} --schedule {schedule} --no-cpu-baseline"
+
+
+def sq_commands(workload: str, schedule: str, out: str = "OUT", bench_args: str = "") -> list:
     """The one counter pass that sq_summary() reads."""
     return [f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {out}/sq -o run -- python -u bench.py "
-            f"--workload {workload} --schedule {schedule} --no-cpu-baseline --steps 5 --warmup 2"]
+            f"{_bench_args(workload, schedule, bench_args)} --steps 5 --warmup 2"]
 
 
-def sq_summary(out: str, workload: str, schedule: str = "balanced") -> str:
-    """profiles/counters_<schedule>_<workload>.md: per kernel of the step, instructions per wave, the
-    MFMA pipe's busy share per SIMD, the share of wave cycles spent waiting, LDS bank conflicts."""
+def _per_kernel(path: str):
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     meta = {}
-    for r in csv.DictReader(open(os.path.join(out, "sq", "run_counter_collection.csv"))):
+    for r in csv.DictReader(open(path)):
         k = r["Kernel_Name"]
-        if not any(t in k for t in ("pa_decode", "pa_prefix", "pa_reduce", "kv_write")):
+        if not any(t in k for t in OUR_KERNELS):
             continue
         vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
         meta[k] = int(r["Grid_Size"])
-    lines = [f"# {workload}: core counters of the benchmark step ({schedule} schedule)", "",
+    return vals, meta
+
+
+def sq_summary(out: str, workload: str, schedule: str = "balanced", bench_args: str = "", name: str = "") -> str:
+    """profiles/counters_<name or schedule_workload>.md: per kernel of the step, instructions per
+    wave, the MFMA pipe's busy share per SIMD, the share of wave cycles spent waiting, LDS bank
+    conflicts."""
+    vals, meta = _per_kernel(os.path.join(out, "sq", "run_counter_collection.csv"))
+    name = name or f"{schedule}_{workload}"
+    lines = [f"# {workload}: core counters of the benchmark step ({bench_args or schedule + ' schedule'})", "",
              f"Kernel source sha256[:16] = `{source_hash()}` (paged_kv_cache_224_amd/csrc/pagedkv.hip without "
              "comments)", "", "## Commands (run from the repository root on one MI355X; OUT is any scratch folder)",
-             "", "```"] + sq_commands(workload, schedule) + [
+             "", "```"] + sq_commands(workload, schedule, bench_args=bench_args) + [
              f"python -c \"from paged_kv_cache_224_amd.profile_summary import sq_summary; "
-             f"sq_summary('OUT', '{workload}', '{schedule}')\"", "```", "",
+             f"sq_summary('OUT', '{workload}', '{schedule}', '{bench_args}', '{name}')\"", "```", "",
              "Means over the dispatches of the run.  Counters are summed over the whole GPU.  Definitions:",
              "- per wave: an instruction count / (grid threads / 64);",
              "- MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), the share of the CUs' busy "
@@ -190,7 +204,51 @@ def sq_summary(out: str, workload: str, schedule: str = "balanced") -> str:
     lines.append("")
     text = "\n".join(lines)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"counters_{schedule}_{workload}.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"counters_{name}.md"), "w") as fh:
+        fh.write(text)
+    return text
+
+
+# L2 (TCC) hits and misses and the mean resident waves per CU, one pass.
+CACHE_COUNTERS = ["TCC_HIT_sum", "TCC_MISS_sum", "MeanOccupancyPerCU"]
+
+
+def cache_commands(workload: str, schedule: str, out: str = "OUT", bench_args: str = "") -> list:
+    """The one counter pass that cache_summary() reads."""
+    return [f"rocprofv3 --pmc {' '.join(CACHE_COUNTERS)} --output-format csv -d {out}/cache -o run -- python -u "
+            f"bench.py {_bench_args(workload, schedule, bench_args)} --steps 5 --warmup 2"]
+
+
+def cache_summary(out: str, workload: str, schedule: str = "balanced", bench_args: str = "", name: str = "",
+                  waves_per_cu: str = "") -> str:
+    """profiles/cache_<name or schedule_workload>.md: per kernel, the L2 hit rate TCC_HIT / (TCC_HIT +
+    TCC_MISS) and the mean number of waves resident per CU while the GPU is busy."""
+    vals, meta = _per_kernel(os.path.join(out, "cache", "run_counter_collection.csv"))
+    name = name or f"{schedule}_{workload}"
+    lines = [f"# {workload}: L2 hit rate and occupancy of the benchmark step "
+             f"({bench_args or schedule + ' schedule'})", "",
+             f"Kernel source sha256[:16] = `{source_hash()}` (paged_kv_cache_224_amd/csrc/pagedkv.hip without "
+             "comments)", "", "## Commands (run from the repository root on one MI355X; OUT is any scratch folder)",
+             "", "```"] + cache_commands(workload, schedule, bench_args=bench_args) + [
+             f"python -c \"from paged_kv_cache_224_amd.profile_summary import cache_summary; "
+             f"cache_summary('OUT', '{workload}', '{schedule}', '{bench_args}', '{name}')\"", "```", "",
+             "Means over the dispatches of the run.  L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) "
+             "over all L2 channels (uncached reads count as misses).  MeanOccupancyPerCU = accumulated "
+             "SQ_LEVEL_WAVES / GRBM_GUI_ACTIVE / CUs: waves resident per CU, averaged over the kernel's busy time "
+             "(a CU holds at most 32 waves; the resident limit of each kernel follows from its workgroup size, "
+             "registers and LDS).", "",
+             "| kernel | waves in the grid | L2 hits | L2 misses | L2 hit rate | mean waves per CU |",
+             "|---|---|---|---|---|---|"]
+    for k in sorted(vals):
+        m = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        hit, miss = m.get("TCC_HIT_sum", 0.0), m.get("TCC_MISS_sum", 0.0)
+        rate = hit / (hit + miss) if hit + miss else 0.0
+        lines.append(f"| {k[:80]} | {max(1, meta[k] // 64)} | {hit:.0f} | {miss:.0f} | {100 * rate:.1f}% | "
+                     f"{m.get('MeanOccupancyPerCU', 0.0):.2f} |")
+    lines.append("")
+    text = "\n".join(lines)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"cache_{name}.md"), "w") as fh:
         fh.write(text)
     return text
 
