@@ -175,3 +175,47 @@ def test_random_append(seed):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
     assert torch.equal(pools[0][0].view(torch.uint8), kc_ref.view(torch.uint8))
     assert max_err(outs[0].float().numpy(), ref) <= tolerance(cfg)
+
+
+TILED_SEEDS = _seeds("PKV_RANDOM_TILED_SEEDS", 0, 40)
+
+
+@pytest.mark.parametrize("seed", TILED_SEEDS)
+def test_random_multi_query_tiled(seed):
+    """paged_attn_multi_query with more (head, new token) columns than one MFMA tile (the tiled
+    kernel): random shapes, dtypes, lengths (the turnover values too), shared first blocks and
+    schedules, with q_len drawn so that G * q_len > 16, up to several column blocks."""
+    cfg, lens, share, sched, W, _ = _draw(700 + seed)
+    rng = np.random.default_rng(5000 + seed)
+    G = cfg.group
+    L = int(rng.integers(16 // G + 1, max(16 // G + 2, min(48, 512 // G) + 1)))
+    B = min(cfg.B, 10)
+    maxL = min(cfg.max_len, 900)
+    cfg = dataclasses.replace(cfg, B=B, max_len=maxL, lens=("uniform", maxL, maxL))
+    lens = np.clip(lens[:B], 0, maxL).astype(np.int32)
+    w = I.make_workload(cfg)
+    bt = w.block_tables.copy()
+    share = min(share, bt.shape[1])
+    if share:
+        bt[1:, :share] = bt[0, :share]
+    w = dataclasses.replace(w, context_lens=lens, block_tables=bt)
+    kvt = torch.uint8 if cfg.kv_dtype == "fp8" else I.DTYPES[cfg.kv_dtype]
+    PS = [0, cfg.partition_size, pk.multi_query_split(cfg.Hq, cfg.Hkv, cfg.D, L, I.DTYPES[cfg.q_dtype], kvt),
+          -W][sched]
+    print(f"[random tiled {seed}] Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} BS={cfg.block_size} "
+          f"{cfg.q_dtype}/{cfg.kv_dtype} B={B} max={maxL} share={share} PS={PS} L={L} lens={lens.tolist()}",
+          flush=True)
+    kc_ref, vc_ref = _oracle_pools(w)
+    kvdt = "fp8" if cfg.kv_dtype == "fp8" else None
+    q = I.multi_query_q(cfg, L, seed=seed)
+    mref = oracle.attn_multi_query(q, kc_ref, vc_ref, bt, lens, w.scale, w.k_scale, w.v_scale, kvdt)
+    kc, vc = gpu_pools(w, write_step=False)
+    ws = pk.DecodeWorkspace(B, L * cfg.Hq, cfg.D, maxL, PS, device=DEV)
+    out = torch.full((B, L, cfg.Hq, cfg.D), float("nan"), dtype=I.DTYPES[cfg.q_dtype], device=DEV)
+    pk.multi_query(out, q.to(DEV), kc, vc, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV), w.scale,
+                   ws, w.k_scale, w.v_scale, shared_blocks=bool(share))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert max_err(got, mref) <= tolerance(cfg)
+    for b, n in enumerate(lens.tolist()):
+        assert np.all(got[b, :max(0, L - n)] == 0)

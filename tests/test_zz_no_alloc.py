@@ -91,3 +91,29 @@ def test_noalloc_rejects_calls_beyond_the_scratch():
         pk.paged_attn_decode_noalloc(out, q, kc, kc, bt, lens, 0.1, 128, -256)
     assert e.value.status == -12
     assert cfg.Hkv == 8
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_noalloc_random_draws(seed):
+    """Random shapes, dtype pairs, lengths and widths (the draws of the randomized decode tests):
+    bit-equal to decode + reduce with a caller workspace, and within the oracle's tolerance."""
+    import oracle
+    from test_gpu_random import _draw, _oracle_pools
+    cfg, lens, share, _, W, _ = _draw(900 + seed)
+    w = I.make_workload(cfg)
+    bt = w.block_tables.copy()
+    if share:
+        bt[1:, :share] = bt[0, :share]
+    w = dataclasses.replace(w, context_lens=lens, block_tables=bt)
+    kvt = torch.uint8 if cfg.kv_dtype == "fp8" else I.DTYPES[cfg.kv_dtype]
+    PS = pk.balanced_split(cfg.Hkv, cfg.D, I.DTYPES[cfg.q_dtype], kvt) if seed % 2 else -W
+    _say(f"[noalloc random {seed}] Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} BS={cfg.block_size} "
+         f"{cfg.q_dtype}/{cfg.kv_dtype} B={cfg.B} max={cfg.max_len} PS={PS}")
+    kc_ref, vc_ref = _oracle_pools(w)
+    kvdt = "fp8" if cfg.kv_dtype == "fp8" else None
+    ref = oracle.attn(w.q, kc_ref, vc_ref, bt, lens, w.scale, w.k_scale, w.v_scale, kvdt)
+    kc, vc = gpu_pools(w, write_step=False)
+    got = _noalloc(w, kc, vc, PS, cfg.max_len)
+    want = gpu_decode(w, kc, vc, PS, max_context_len=cfg.max_len, shared_blocks=bool(share))
+    assert np.array_equal(got, want)
+    assert max_err(got, ref) <= tolerance(cfg)
