@@ -368,7 +368,7 @@ def multi_query_op(args):
     tflops = flops / kern / 1e12
     mfma_peak = 2500.0                                  # dense bf16 / f16 MFMA, TFLOP/s
     hbm_frac, mfma_frac = gbps / HBM_PEAK_GBPS, tflops / mfma_peak
-    tiled = cfg.group * L > 16
+    tiled = cfg.group * L > 32
     res = {"metric": "multi-query paged attention KV GB/s and query tokens/s", "value": round(gbps, 1),
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -384,7 +384,7 @@ def multi_query_op(args):
                         "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
                         "frac": round(max(hbm_frac, mfma_frac), 4), "hbm_frac": round(hbm_frac, 4),
                         "mfma_frac": round(mfma_frac, 4), "traffic": None,
-                        "kernel": "pa_mq_tiled_kernel" if tiled else "pa_decode_kernel",
+                        "kernel": "pa_mq_tiled_kernel" if tiled else ("pa_decode_kernel, two column tiles per wave" if cfg.group * L > 16 else "pa_decode_kernel"),
                         "bytes_per_launch": moved}}
     print(json.dumps(res), flush=True)
 

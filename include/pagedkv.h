@@ -177,10 +177,10 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
  *   sequence ([num_seqs, q_len, num_heads, Pslots, ...]); paged_attn_reduce called with
  *   num_heads = q_len * num_heads forms `out`.
  * Every other argument, the supported set and the error behaviour are those of
- * paged_attn_decode, plus 1 <= q_len <= 4096.  Kernels: with G * q_len <= 16 (G = num_heads /
- * num_kv_heads) the (head, new token) pairs of a KV group fill one MFMA tile and the decode
- * kernel streams the cache once for them; with more pairs a tiled kernel stages 64-token K/V
- * blocks in LDS and scores them against up to 128 pairs per workgroup on the matrix cores
+ * paged_attn_decode, plus 1 <= q_len <= 4096.  Kernels: with G * q_len <= 32 (G = num_heads /
+ * num_kv_heads) the (head, new token) pairs of a KV group fill one or two MFMA tiles of a decode
+ * wave, which streams the cache once for them; with more pairs a tiled kernel stages 64-token
+ * K/V blocks in LDS and scores them against up to 128 pairs per workgroup on the matrix cores
  * (paged_attn_multi_query_split() gives the balanced W that fills the device for it).
  */
 int paged_attn_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -409,7 +409,7 @@ int paged_attn_balanced_split(int num_kv_heads, int head_dim, int q_dtype, int k
 
 /* partition_size (negative) of the balanced split that fills the current HIP device for
    paged_attn_multi_query with q_len new tokens: paged_attn_balanced_split() when
-   (num_heads / num_kv_heads) * q_len <= 16, else about one tiled workgroup per compute unit.
+   (num_heads / num_kv_heads) * q_len <= 32, else about one tiled workgroup per compute unit.
    Returns 0 if no device is available or the shape is unsupported.  Queries the device. */
 int paged_attn_multi_query_split(int num_heads, int num_kv_heads, int head_dim, int q_len, int q_dtype,
                                  int kv_dtype);

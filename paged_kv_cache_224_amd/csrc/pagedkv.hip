@@ -281,8 +281,8 @@ struct DecodeParams {
   float v_scale;
 };
 
-// Compile-time geometry of one 16-token tile.
-template <int D, int KV>
+// Compile-time geometry of one 16-token tile for a wave of CT 16-column tiles.
+template <int D, int KV, int CT = 1>
 struct Tile {
   static constexpr int ESZ = (KV == KFP8) ? 1 : 2;         // bytes per cached element
   static constexpr int ROWB = D * ESZ;                      // bytes of one (token, head) row
@@ -294,7 +294,7 @@ struct Tile {
   static constexpr int TPI = 64 / CPRS;                     // tokens covered by one V load
   static constexpr int CPR = D / 8;                         // 16-byte chunks per LDS row (16-bit)
   static constexpr int VLDS = 16 * D * 2;                   // the V tile
-  static constexpr int QLDS = NS * 64 * 16;                 // one segment's q operand
+  static constexpr int QLDS = CT * NS * 64 * 16;            // one segment's q operands
   static constexpr int LDS_BYTES = VLDS + QLDS;             // per wave
   // Tiles in flight per wave.  An fp8 tile is half the bytes of a 16-bit one, so it keeps
   // two in flight to hold the same bytes per wave against the load latency.
@@ -480,11 +480,14 @@ __device__ __forceinline__ bool balanced_start(SegSource& src, Seg& cur, const i
 // wave that streams the tile holding position n - 1 fetches the new K/V row of its head
 // together with that tile's loads, uses it in place of the stale pool row and stores it into
 // the pool; no other workgroup reads that slot during the launch.
-template <int D, int KV, bool BF, int MODE, int POLICY, bool APPEND = false>
+//
+// CT > 1 (multi-query with 17 .. 16 * CT (head, new token) columns per KV group): each wave carries
+// CT tiles of 16 MFMA columns; every K and V operand it loads feeds all CT tiles.
+template <int D, int KV, bool BF, int MODE, int POLICY, bool APPEND = false, int CT = 1>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_decode_kernel(DecodeParams a) {
-  using TL = Tile<D, KV>;
-  static_assert(!APPEND || (KV != KFP8 && TL::PF == 1), "append is for 16-bit caches, one tile in flight");
+  using TL = Tile<D, KV, CT>;
+  static_assert(!APPEND || (KV != KFP8 && TL::PF == 1 && CT == 1), "append is for 16-bit caches, one tile in flight");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -558,13 +561,19 @@ void pa_decode_kernel(DecodeParams a) {
   // ---- per-lane constants
   // MFMA column hh = (query head hh / L of the group, new query token hh % L).  Token i of the
   // L new tokens sits at position n - L + i and sees the first n - (L - 1 - i) tokens.
+  // Tile c holds columns 16 c .. 16 c + 15.
   const int hh = lane & 15;
   const int grp = lane >> 4;    // MFMA row group
-  const bool hvalid = hh < a.G * a.L;
-  const int hsel = hvalid ? hh : 0;
-  const int qi = hsel % a.L;
-  const int hoff = g * a.G + hsel / a.L;
-  const int hidden = a.L - 1 - qi;                      // newer tokens this column must not see
+  bool hvalid[CT];
+  int qi[CT], hoff[CT], hidden[CT];                     // hidden: newer tokens the column must not see
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    hvalid[c] = 16 * c + hh < a.G * a.L;
+    const int hsel = hvalid[c] ? 16 * c + hh : 0;
+    qi[c] = hsel % a.L;
+    hoff[c] = g * a.G + hsel / a.L;
+    hidden[c] = a.L - 1 - qi[c];
+  }
   const int rowstride = a.Hkv * TL::ROWB;               // bytes between consecutive tokens
   int koff[TL::KLD];
 #pragma unroll
@@ -606,16 +615,19 @@ void pa_decode_kernel(DecodeParams a) {
   // q of sequence b as the B operand of S^T = K . Q^T, d order matching the K loads.  Lanes
   // of MFMA columns >= G load a valid head of the group: those columns are computed and
   // dropped, and no select on the loaded value forces a wait right after the loads.
-  auto load_q = [&](int b, u32x4* qv) {
-    const char* qrow = (const char*)a.q + (((size_t)b * a.L + qi) * a.Hq + hoff) * D * 2;
+  auto load_q = [&](int b, u32x4 (*qv)[TL::NS]) {
 #pragma unroll
-    for (int s = 0; s < TL::NS; ++s) {
-      int d0;
-      if constexpr (KV == KFP8)
-        d0 = 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
-      else
-        d0 = 32 * s + 8 * grp;
-      qv[s] = *(const u32x4*)(qrow + d0 * 2);
+    for (int c = 0; c < CT; ++c) {
+      const char* qrow = (const char*)a.q + (((size_t)b * a.L + qi[c]) * a.Hq + hoff[c]) * D * 2;
+#pragma unroll
+      for (int s = 0; s < TL::NS; ++s) {
+        int d0;
+        if constexpr (KV == KFP8)
+          d0 = 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
+        else
+          d0 = 32 * s + 8 * grp;
+        qv[c][s] = *(const u32x4*)(qrow + d0 * 2);
+      }
     }
   };
   // Physical block of logical tile `tile` of sequence b (a wave-uniform address).  A valid
@@ -646,13 +658,16 @@ void pa_decode_kernel(DecodeParams a) {
   };
 
   // ---- softmax / accumulator state of the current segment
-  f32x4 acc[TL::NT];
-  float m, lsum;
+  f32x4 acc[CT][TL::NT];
+  float m[CT], lsum[CT];
   auto reset = [&]() {
 #pragma unroll
-    for (int T = 0; T < TL::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    lsum = 0.f;
+    for (int c = 0; c < CT; ++c) {
+#pragma unroll
+      for (int T = 0; T < TL::NT; ++T) acc[c][T] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[c] = -INFINITY;
+      lsum[c] = 0.f;
+    }
   };
   reset();
 
@@ -660,8 +675,9 @@ void pa_decode_kernel(DecodeParams a) {
   // registers are free, so the next tile's loads can land in them.  Rows >= n of a sequence's
   // last tile arrive as zeros (their loads are out of the tile's buffer range), so stale bytes,
   // which may be NaN, never reach the scores or the V tile.
-  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4* qv) -> f32x4 {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  auto part1 = [&](const u32x4* kr, const u32x4* vr, const u32x4 (*qv)[TL::NS], f32x4* s) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) s[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < TL::NS; ++st) {
       u32x4 kop;
@@ -672,7 +688,8 @@ void pa_decode_kernel(DecodeParams a) {
       } else {
         kop = kr[st];
       }
-      s = mfma_16x16x32<BF>(kop, qv[st], s);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) s[c] = mfma_16x16x32<BF>(kop, qv[c][st], s[c]);
     }
 #pragma unroll
     for (int r = 0; r < TL::VLD; ++r) {
@@ -681,7 +698,6 @@ void pa_decode_kernel(DecodeParams a) {
       else
         *(u32x4*)(vtile + vslot[r]) = vr[r];
     }
-    return s;
   };
 
   // Second half: online softmax (exp2 domain) and O^T += V^T . P^T.  Tokens a column may not
@@ -689,66 +705,74 @@ void pa_decode_kernel(DecodeParams a) {
   // every column sees whole (all but the last tile or two of a segment) skips the selects.  A
   // column that has seen no token yet keeps m = -inf; its probabilities are computed against
   // 0 so that they come out 0, not NaN.
-  auto part2 = [&](int tile, int n, f32x4 s) {
+  auto part2 = [&](int tile, int n, const f32x4* s) {
     const int tbase = (tile << 4) + 4 * grp;
-    float x[4];
-    if (((tile + 1) << 4) <= n - (a.L - 1)) {
+    const bool whole = ((tile + 1) << 4) <= n - (a.L - 1);   // every column sees the whole tile
+    u32x2 pop[CT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = s[e] * a.c2;
-    } else {
-      const int lim = n - hidden;
+    for (int c = 0; c < CT; ++c) {
+      float x[4];
+      if (whole) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (tbase + e < lim) ? s[e] * a.c2 : -INFINITY;
+        for (int e = 0; e < 4; ++e) x[e] = s[c][e] * a.c2;
+      } else {
+        const int lim = n - hidden[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (tbase + e < lim) ? s[c][e] * a.c2 : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = max_rows32(max_rows16(mx));
+      if (__ballot(mx > m[c]) != 0) {
+        // every lane rescales when any column's maximum rises; a column that has seen no token
+        // yet (m = -inf, possible under the causal mask) has nothing to rescale
+        const float mn = fmaxf(m[c], mx);
+        const float alpha = m[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - mn);
+        m[c] = mn;
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int T = 0; T < TL::NT; ++T) acc[c][T] *= alpha;
+      }
+      unsigned short ph[4];
+      const float mb = m[c] == -INFINITY ? 0.f : m[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[e] - mb));
+        lsum[c] += from16<BF>(ph[e]);
+      }
+      pop[c] = u32x2{pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
     }
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = max_rows32(max_rows16(mx));
-    if (__ballot(mx > m) != 0) {
-      // every lane rescales when any column's maximum rises; a column that has seen no token
-      // yet (m = -inf, possible under the causal mask) has nothing to rescale
-      const float mn = fmaxf(m, mx);
-      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int T = 0; T < TL::NT; ++T) acc[T] *= alpha;
-    }
-    unsigned short ph[4];
-    const float mb = m == -INFINITY ? 0.f : m;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ph[e] = f32_to_16<BF>(__builtin_amdgcn_exp2f(x[e] - mb));
-      lsum += from16<BF>(ph[e]);
-    }
-    const u32x2 pop = {pack2(ph[0], ph[1]), pack2(ph[2], ph[3])};
 #pragma unroll
     for (int T = 0; T < TL::NT; ++T) {
       s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)vtile + troff[T]));
-      acc[T] = mfma_16x16x16<BF>(__builtin_bit_cast(u32x2, raw), pop, acc[T]);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[c][T] = mfma_16x16x16<BF>(__builtin_bit_cast(u32x2, raw), pop[c], acc[c][T]);
     }
   };
 
   // Total sum over the 4 row groups, normalise, store the row or the partial.
   auto finalize = [&](const Seg& sg) {
-    const float l = sum_rows32(sum_rows16(lsum));
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
-    if (hvalid) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const float l = sum_rows32(sum_rows16(lsum[c]));
+      const float inv = l > 0.f ? a.v_scale / l : 0.f;
+      if (!hvalid[c]) continue;
       if constexpr (MODE == MODE_SINGLE) {
-        unsigned short* orow = (unsigned short*)a.out + (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * D;
+        unsigned short* orow = (unsigned short*)a.out + (((size_t)sg.b * a.L + qi[c]) * a.Hq + hoff[c]) * D;
 #pragma unroll
         for (int T = 0; T < TL::NT; ++T) {
           u32x2 wv;
-          wv.x = pack2(f32_to_16<BF>(acc[T][0] * inv), f32_to_16<BF>(acc[T][1] * inv));
-          wv.y = pack2(f32_to_16<BF>(acc[T][2] * inv), f32_to_16<BF>(acc[T][3] * inv));
+          wv.x = pack2(f32_to_16<BF>(acc[c][T][0] * inv), f32_to_16<BF>(acc[c][T][1] * inv));
+          wv.y = pack2(f32_to_16<BF>(acc[c][T][2] * inv), f32_to_16<BF>(acc[c][T][3] * inv));
           *(u32x2*)(orow + 16 * T + 4 * grp) = wv;
         }
       } else if (sg.slot >= 0 && (a.compact || a.slot0 + sg.slot < a.Pslots)) {
-        const size_t prow = a.compact ? (size_t)(sg.b + src.w) * a.L * a.Hq + (size_t)qi * a.Hq + hoff
-                                      : (((size_t)sg.b * a.L + qi) * a.Hq + hoff) * a.Pslots + a.slot0 + sg.slot;
+        const size_t prow = a.compact ? (size_t)(sg.b + src.w) * a.L * a.Hq + (size_t)qi[c] * a.Hq + hoff[c]
+                                      : (((size_t)sg.b * a.L + qi[c]) * a.Hq + hoff[c]) * a.Pslots + a.slot0 + sg.slot;
         float* orow = a.tmp_out + prow * D;
 #pragma unroll
-        for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[T] * inv;
+        for (int T = 0; T < TL::NT; ++T) *(f32x4*)(orow + 16 * T + 4 * grp) = acc[c][T] * inv;
         if (grp == 0) {
-          a.max_logits[prow] = m * kLn2;
+          a.max_logits[prow] = m[c] * kLn2;
           a.exp_sums[prow] = l;
         }
       }
@@ -766,7 +790,7 @@ void pa_decode_kernel(DecodeParams a) {
   // the tiles in flight), and read back into qc at the next switch.  Registers loaded from
   // memory are never copied, which would force a wait right after the load.
   Seg nxt = src.next(cur, lane);
-  u32x4 qc[TL::NS], qn[TL::NS];
+  u32x4 qc[CT][TL::NS], qn[CT][TL::NS];
   load_q(cur.b, qc);
   bool qpend = nxt.valid;
   if (qpend) load_q(nxt.b, qn);
@@ -869,14 +893,17 @@ void pa_decode_kernel(DecodeParams a) {
           if (vl) *(u32x4*)((char*)vbase + apoff + (lane % TL::CPRS) * 16) = vnew;
         }
       }
-      const f32x4 sc = part1(kr[r], vr[r], qc);
+      f32x4 sc[CT];
+      part1(kr[r], vr[r], qc, sc);
       __builtin_amdgcn_sched_barrier(0);
       issue(kr[r], vr[r]);                              // set r is free again
       __builtin_amdgcn_sched_barrier(0);
       part2(tile, cur.n, sc);
       if (qpend) {
 #pragma unroll
-        for (int s = 0; s < TL::NS; ++s) *(u32x4*)(qstage + (s * 64 + lane) * 16) = qn[s];
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int s = 0; s < TL::NS; ++s) *(u32x4*)(qstage + ((c * TL::NS + s) * 64 + lane) * 16) = qn[c][s];
         qpend = false;
       }
       if (tile + 1 < cur.thi) {
@@ -892,7 +919,9 @@ void pa_decode_kernel(DecodeParams a) {
       reset();
       cur = nxt;
 #pragma unroll
-      for (int s = 0; s < TL::NS; ++s) qc[s] = *(const u32x4*)(qstage + (s * 64 + lane) * 16);
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int s = 0; s < TL::NS; ++s) qc[c][s] = *(const u32x4*)(qstage + ((c * TL::NS + s) * 64 + lane) * 16);
       nxt = src.next(cur, lane);
       qpend = nxt.valid;
       if (qpend) load_q(nxt.b, qn);
@@ -1720,21 +1749,26 @@ int slots_of(int max_context_len, int partition_size) {
 int waves_per_group(int Hkv) { return Hkv < kMaxWaves ? Hkv : kMaxWaves; }
 int head_groups(int Hkv) { return (Hkv + kMaxWaves - 1) / kMaxWaves; }
 
-template <int D, int KV, bool BF, int POLICY>
+template <int D, int KV, bool BF, int POLICY, int CT>
 void launch_decode_policy(const DecodeParams& p, bool last, hipStream_t st) {
   const int HG = head_groups(p.Hkv);
   const int nw = waves_per_group(p.Hkv);
-  const size_t lds = (size_t)nw * Tile<D, KV>::LDS_BYTES;
+  const size_t lds = (size_t)nw * Tile<D, KV, CT>::LDS_BYTES;
   if (p.mode == MODE_SINGLE)
-    launch(pa_decode_kernel<D, KV, BF, MODE_SINGLE, POLICY>, dim3(p.B, HG), dim3(64 * nw), lds, st, last, p);
-  else if (p.mode == MODE_FIXED)
-    launch(pa_decode_kernel<D, KV, BF, MODE_FIXED, POLICY>, dim3(p.Pslots, HG, p.B), dim3(64 * nw), lds, st, last,
+    launch(pa_decode_kernel<D, KV, BF, MODE_SINGLE, POLICY, false, CT>, dim3(p.B, HG), dim3(64 * nw), lds, st, last,
            p);
+  else if (p.mode == MODE_FIXED)
+    launch(pa_decode_kernel<D, KV, BF, MODE_FIXED, POLICY, false, CT>, dim3(p.Pslots, HG, p.B), dim3(64 * nw), lds, st,
+           last, p);
   else
-    launch(pa_decode_kernel<D, KV, BF, MODE_BALANCED, POLICY>, dim3(p.W, HG), dim3(64 * nw), lds, st, last, p);
+    launch(pa_decode_kernel<D, KV, BF, MODE_BALANCED, POLICY, false, CT>, dim3(p.W, HG), dim3(64 * nw), lds, st, last,
+           p);
 }
 
-// Multi-query with more (head, new token) columns than one MFMA tile holds: the tiled kernel,
+// Columns (head, new token) per KV group that the decode kernel carries (two MFMA tiles per wave).
+constexpr int kDecodeMaxCols = 32;
+
+// Multi-query with more (head, new token) columns than a decode wave carries: the tiled kernel,
 // one workgroup per (work item, KV head, block of kMqCols columns).  Eight waves of one
 // 16-column tile, two waves per SIMD: measured faster than four waves (one per SIMD) of two
 // tiles each, and than four-wave workgroups of one tile, at every q_len tried.
@@ -1785,12 +1819,17 @@ void launch_decode_append(const DecodeParams& p, bool shared_blocks, hipStream_t
            true, p);
 }
 
+// Up to 16 (head, new token) columns per KV group: one MFMA tile per wave; up to 32: two.
 template <int D, int KV, bool BF>
 void launch_decode(const DecodeParams& p, bool shared_blocks, bool last, hipStream_t st) {
-  if (shared_blocks)
-    launch_decode_policy<D, KV, BF, kCachedPolicy>(p, last, st);
-  else
-    launch_decode_policy<D, KV, BF, kStreamPolicy>(p, last, st);
+  const bool two = p.G * p.L > 16;
+  if (shared_blocks) {
+    if (two) launch_decode_policy<D, KV, BF, kCachedPolicy, 2>(p, last, st);
+    else launch_decode_policy<D, KV, BF, kCachedPolicy, 1>(p, last, st);
+  } else {
+    if (two) launch_decode_policy<D, KV, BF, kStreamPolicy, 2>(p, last, st);
+    else launch_decode_policy<D, KV, BF, kStreamPolicy, 1>(p, last, st);
+  }
 }
 
 template <int D, int KV, bool BF>
@@ -2079,7 +2118,7 @@ static void launch_decode_dt(const DecodeParams& p, int head_dim, int q_dtype, i
                              hipStream_t st) {
   const bool bf = q_dtype == PKV_BF16;
   const bool f8 = kv_dtype == PKV_FP8_E4M3;
-  if (p.G * p.L > 16) {                                     // more columns than one MFMA tile
+  if (p.G * p.L > kDecodeMaxCols) {                        // more columns than a decode wave carries
     if (head_dim == 128) {
       if (f8) { if (bf) launch_mq_tiled<128, KFP8, true>(p, last, st); else launch_mq_tiled<128, KFP8, false>(p, last, st); }
       else    { if (bf) launch_mq_tiled<128, KBF16, true>(p, last, st); else launch_mq_tiled<128, KF16, false>(p, last, st); }
@@ -2337,7 +2376,7 @@ int paged_attn_multi_query_split(int num_heads, int num_kv_heads, int head_dim, 
       q_len > kMaxQueryLen || (head_dim != 64 && head_dim != 128))
     return 0;
   const int G = num_heads / num_kv_heads;
-  if (G * q_len <= 16) return paged_attn_balanced_split(num_kv_heads, head_dim, q_dtype, kv_dtype);
+  if (G * q_len <= kDecodeMaxCols) return paged_attn_balanced_split(num_kv_heads, head_dim, q_dtype, kv_dtype);
   int dev = 0;
   hipDeviceProp_t prop;
   if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;

@@ -1,6 +1,6 @@
 """GPU parity of paged_attn_multi_query past one MFMA tile of (head, new token) columns
-(G * L > 16: chunked prefill, long draft verification), which runs the tiled kernel, against
-the fp64 oracle.  All three schedules, the Llama-3-8B (G = 4, bf16) and Llama-3-70B (G = 8, fp8
+(G * L > 16: chunked prefill, long draft verification) against the fp64 oracle: up to 32 columns
+the decode wave carries two tiles, beyond that the tiled kernel runs.  All three schedules, the Llama-3-8B (G = 4, bf16) and Llama-3-70B (G = 8, fp8
 cache) shapes at L = 8, 16 and 64, contexts shorter than L, odd L, G = 1 and G = 16, and
 sampled rows of the full-size batches in the configuration the benchmark times."""
 import dataclasses
