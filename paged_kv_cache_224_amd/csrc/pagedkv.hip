@@ -1632,6 +1632,92 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(void* out, const float* 
   }
 }
 
+// Merge for launches with many output rows and few partials per row (multi-query: L * Hq rows
+// per sequence, a narrow balanced split): each 16-lane group of a wave folds all partials of
+// its own row, so a wave serves four rows instead of one.  Needs rows_per_seq >= 4, so the four
+// rows of a wave belong to at most two consecutive sequences.  Same partial layout and the same
+// partial counts as pa_reduce_kernel (non-compact layout).
+template <int D, bool BF>
+__global__ __launch_bounds__(256) void pa_reduce_rows_kernel(void* out, const float* tmp_out,
+                                                            const float* max_logits, const float* exp_sums,
+                                                            const int32_t* lens, int B, int Hq, int Pslots,
+                                                            int PS, int cap, int t0, int slot0) {
+  constexpr int DPL = D / 16;                 // output elements per lane (8 or 4)
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, l16 = lane & 15;
+  const int r0 = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 4;
+  if (r0 >= B * Hq) return;
+  const int row = r0 + grp;                   // this group's row (b * Hq + h)
+  const bool live = row < B * Hq;
+  const int b_lo = r0 / Hq;                   // the wave's first sequence
+  const int b = live ? row / Hq : b_lo;       // b_lo or b_lo + 1
+  const int n = clamp_len(lens[b], cap);
+  int P, first_range = 0;
+  if (PS > 0) {
+    P = (n + PS - 1) / PS;
+  } else {
+    int total = 0, before = 0;               // split units of the whole batch, of sequences < b_lo
+    for (int i0 = 0; i0 < B; i0 += 64) {
+      const int i = i0 + lane;
+      const int u = i < B ? units_after(clamp_len(lens[i], cap), t0) : 0;
+      total += u;
+      before += i < b_lo ? u : 0;
+    }
+    total = __builtin_amdgcn_readlane(wave_incl_scan(total), 63);
+    before = __builtin_amdgcn_readlane(wave_incl_scan(before), 63);
+    if (b > b_lo) before += units_after(clamp_len(__builtin_amdgcn_readfirstlane(lens[b_lo]), cap), t0);
+    const int nt = tiles_after(n, t0);
+    if (nt == 0) {
+      P = 0;
+    } else {
+      const Split split(total, -PS);
+      const int first = before + 1;          // the unit of b's first tile
+      first_range = split.owner(first);
+      P = split.owner(first + nt - 1) - first_range + 1;
+    }
+  }
+  P = live ? min(slot0 + P, Pslots) : 0;
+  const float* ml = max_logits + (size_t)row * Pslots;
+  const float* es = exp_sums + (size_t)row * Pslots;
+  const float* to = tmp_out + (size_t)row * Pslots * D + l16 * DPL;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  float mrun = -INFINITY, wrun = 0.f;
+#pragma unroll 2
+  for (int p = 0; p < P; ++p) {
+    const float mp = ml[p] * kLog2e;
+    const float lp = es[p];
+    float o[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; i += 4) {
+      const f32x4 v = *(const f32x4*)(to + (size_t)p * D + i);
+      o[i] = v[0];
+      o[i + 1] = v[1];
+      o[i + 2] = v[2];
+      o[i + 3] = v[3];
+    }
+    // a partial that saw no token (causal multi-query) has m = -inf and l = 0
+    const float mn = fmaxf(mrun, mp);
+    const float so = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float sn = mp == -INFINITY ? 0.f : lp * __builtin_amdgcn_exp2f(mp - mn);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * so + o[i] * sn;
+    wrun = wrun * so + sn;
+    mrun = mn;
+  }
+  if (!live) return;
+  const float inv = wrun > 0.f ? 1.0f / wrun : 0.f;
+  unsigned w[DPL / 2];
+#pragma unroll
+  for (int i = 0; i < DPL / 2; ++i) w[i] = pack2(f32_to_16<BF>(acc[2 * i] * inv), f32_to_16<BF>(acc[2 * i + 1] * inv));
+  unsigned short* orow = (unsigned short*)out + (size_t)row * D + l16 * DPL;
+  if constexpr (DPL == 8)
+    *(u32x4*)orow = u32x4{w[0], w[1], w[2], w[3]};
+  else
+    *(u32x2*)orow = u32x2{w[0], w[1]};
+}
+
 // ------------------------------------------------------------------ KV write scatter
 
 // Row i of key/value (row_elems elements each) into slot s of the caches; the calling
@@ -1840,11 +1926,23 @@ void launch_prefix(const PrefixParams& p, hipStream_t st) {
   launch(pa_prefix_kernel<D, KV, BF, kPrefixWaves, kPrefixCT>, grid, dim3(64 * kPrefixWaves), lds, st, false, p);
 }
 
+// Output rows from which a merge serves four rows per wave (pa_reduce_rows_kernel).
+constexpr long long kReduceRowsPerGroupMin = 16384;
+
 void launch_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
                    const int32_t* lens, int B, int rows_per_seq, int D, int Pslots, int PS, int cap,
                    int t0, int slot0, bool bf, hipStream_t st, int compact = 0) {
-  const dim3 grid((unsigned)(((long long)B * rows_per_seq + 3) / 4)), block(256);
+  const long long rows = (long long)B * rows_per_seq;
   const int Pm = Pslots > 0 ? Pslots : 1;
+  if (!compact && rows_per_seq >= 4 && rows >= kReduceRowsPerGroupMin) {
+    const dim3 grid((unsigned)((rows + 15) / 16)), block(256);
+    auto k = D == 128 ? (bf ? pa_reduce_rows_kernel<128, true> : pa_reduce_rows_kernel<128, false>)
+                      : (bf ? pa_reduce_rows_kernel<64, true> : pa_reduce_rows_kernel<64, false>);
+    launch(k, grid, block, 0, st, true, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0,
+           slot0);
+    return;
+  }
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   auto k = D == 128 ? (bf ? pa_reduce_kernel<128, true> : pa_reduce_kernel<128, false>)
                     : (bf ? pa_reduce_kernel<64, true> : pa_reduce_kernel<64, false>);
   launch(k, grid, block, 0, st, true, out, tmp_out, max_logits, exp_sums, lens, B, rows_per_seq, Pm, PS, cap, t0,

@@ -125,3 +125,21 @@ def test_tiled_multi_query_is_deterministic_and_block_order_free():
     c = _run(I.permute_blocks(w, seed=11), q, PS, w.cfg.max_len)
     assert np.array_equal(a, b) and np.array_equal(a, c)
     assert dataclasses.is_dataclass(w)
+
+
+def test_many_rows_merge_straddling_sequences():
+    """800 sequences x 7 new tokens x 3 query heads = 16800 output rows, 21 per sequence: the
+    merge serves four rows per wave, and a wave's rows often straddle two sequences, whose
+    balanced-split partial counts differ (G * L = 21: the two-tile decode writes the partials)."""
+    cfg = I.Config("mq_rows", 51, B=800, Hq=3, Hkv=1, D=128, block_size=16, q_dtype="bf16", kv_dtype="bf16",
+                   lens=("uniform", 1, 200), pool=("factor", 1.25), max_len=200, partition_size=64)
+    w = I.make_workload(cfg)
+    L = 7
+    q = I.multi_query_q(cfg, L, seed=12)
+    kc_ref, vc_ref = oracle_pools(w)
+    ref = _oracle(w, q, kc_ref, vc_ref)
+    kc, vc = gpu_pools(w)
+    for PS in (_mq_split(cfg, L), -37, 64):
+        _say(f"[mq many rows] PS={PS}")
+        got = _run(w, q, PS, cfg.max_len, kc, vc)
+        assert max_err(got, ref) <= tolerance(cfg), PS

@@ -391,3 +391,37 @@ def test_length_past_the_table_spoils_only_its_row(mode):
     err = max_err(got[keep], ref[keep])
     _say(f"    other rows max-abs err {err:.3e}")
     assert err <= tolerance(cfg)
+
+
+@pytest.mark.parametrize("B,Hq", [(40, 512), (3300, 5)])
+def test_reduce_alone_many_rows(B, Hq):
+    """A merge with more than 16384 output rows runs one row per 16-lane group (four rows per
+    wave); with 5 rows per sequence a wave's rows straddle two sequences.  Injected partials,
+    NaN garbage past each row's count, against the fp64 merge."""
+    _say(f"[reduce many rows] B={B} Hq={Hq}")
+    rng = np.random.default_rng(9)
+    D, PS = 128, 64
+    lens = rng.integers(0, 300, size=B).astype(np.int32)
+    lens[:3] = [0, 1, 299]
+    maxlen = int(lens.max())
+    Pmax = -(-maxlen // PS)
+    m = rng.normal(0, 3, size=(B, Hq, Pmax)).astype(np.float32)
+    l = rng.uniform(1, 100, size=(B, Hq, Pmax)).astype(np.float32)
+    o = rng.normal(0, 1, size=(B, Hq, Pmax, D)).astype(np.float32)
+    P = -(-lens.astype(np.int64) // PS)
+    for b in range(B):
+        m[b, :, P[b]:] = np.nan
+        l[b, :, P[b]:] = np.nan
+        o[b, :, P[b]:] = np.nan
+    ref = oracle.lse_merge(m.reshape(B * Hq, Pmax), l.reshape(B * Hq, Pmax), o.reshape(B * Hq, Pmax, D),
+                           np.repeat(P, Hq)).reshape(B, Hq, D)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    pk.paged_attn_reduce(out, torch.from_numpy(o).to(DEV), torch.from_numpy(m).to(DEV),
+                         torch.from_numpy(l).to(DEV), torch.from_numpy(lens).to(DEV), maxlen, PS)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    # bf16 keeps 8 significant bits: rounding is at most 2^-8 of the value (single-partition rows
+    # pass normal(0, 1) values through, and a few of 2.6M reach 4 and beyond)
+    assert not np.isnan(got).any()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-3)
+    assert np.all(got[lens == 0] == 0)
