@@ -988,10 +988,16 @@ __device__ __forceinline__ int kslot(int t, int c) {
 // The workgroup's stage pipeline: thread tid moves source chunks tid, tid + 64 * NW, ... of K
 // and of V.  Rows at or past `tend` are zero in LDS.  The block ids of a stage's rows are
 // loaded one stage before its K/V rows, so the row loads never wait on them.
+// Load k of a wave covers chunks 64 * (wave + k * NW) .. + 63, i.e. 64 / CPRS consecutive tokens
+// (4, 8 or 16).  Stage starts are multiples of 16 tokens, so those tokens lie in one 16-token
+// tile and hence in one block: the row address and the buffer range of a K/V load are
+// wave-uniform (scalar), and each lane adds a fixed offset.  (The ids stay per-lane loads: a
+// scalar id load measured slower in the shared-prefix pass.)
 template <int D, int KV, bool BF, int NW>
 struct Stages {
   using SG = StageGeom<D, KV>;
   static constexpr int NLD = (SG::NCH + 64 * NW - 1) / (64 * NW);
+  static constexpr int TPW = 64 / SG::CPRS;                     // tokens per wave and load
   u32x4 kreg[NLD], vreg[NLD];
   int idn[NLD];
 
@@ -1004,20 +1010,30 @@ struct Stages {
     }
   }
   __device__ __forceinline__ void load(const StageSrc& s, int tid, int tok0, int tend) {
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int loff = (lane / SG::CPRS) * s.rowstride + (lane % SG::CPRS) * 16;
     const int bsm1 = (1 << s.bs_shift) - 1;
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
-      const int ci = tid + k * 64 * NW;
-      const int t = ci / SG::CPRS, cs = ci % SG::CPRS;
-      const int tok = tok0 + t;
-      kreg[k] = u32x4{0u, 0u, 0u, 0u};
-      vreg[k] = u32x4{0u, 0u, 0u, 0u};
-      if (ci < SG::NCH && tok < tend) {
-        const unsigned id = min((unsigned)idn[k], s.nbm1);
-        const size_t off = (size_t)id * s.blockbytes + (size_t)(tok & bsm1) * s.rowstride + (size_t)cs * 16;
-        kreg[k] = *(const u32x4*)(s.kc + off);
-        vreg[k] = *(const u32x4*)(s.vc + off);
+      const int ci0 = 64 * (wv + k * NW);
+      if (ci0 >= SG::NCH) {                                     // no chunk of this load (wave-uniform)
+        kreg[k] = u32x4{0u, 0u, 0u, 0u};
+        vreg[k] = u32x4{0u, 0u, 0u, 0u};
+        continue;
       }
+      const int tok = tok0 + ci0 / SG::CPRS;
+      const int nt = tend - tok;                                // tokens of this load below tend
+      // the range ends at the last valid token's row: lanes past it read zeros, no memory access
+      const int span = nt <= 0 ? 0 : (min(nt, TPW) - 1) * s.rowstride + SG::ROWB;
+      const unsigned id = min((unsigned)__builtin_amdgcn_readfirstlane(idn[k]), s.nbm1);
+      const size_t off = (size_t)id * s.blockbytes + (size_t)(tok & bsm1) * s.rowstride;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(s.kc + off), (short)0, span, kBufWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(s.vc + off), (short)0, span, kBufWord3);
+      kreg[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, loff, 0, kCachedPolicy));
+      vreg[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, loff, 0, kCachedPolicy));
     }
   }
   __device__ __forceinline__ void store(char* st, int tid) {
