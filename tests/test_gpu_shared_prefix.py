@@ -172,3 +172,19 @@ def test_checked_mode_rejects_unshared_prefix(monkeypatch):
     assert ei.value.status == -7
     _run(w, kc, vc, 64, 32)                        # the intact table passes the check
     monkeypatch.delenv("PKV_CHECK")
+
+
+def test_many_rows_merge_with_prefix_slots():
+    """1100 rows x 16 query heads = 17600 output rows: the merge takes one row per 16-lane group
+    and reads the prefix pass's slots before the suffix slots (slot0 > 0), over a default and a
+    narrow balanced split."""
+    cfg = _prefix_cfg("tiny", "sp_rows", 1100, 64, 1, 40, seed=29, Hq=16, Hkv=4, q_dtype="bf16", kv_dtype="bf16")
+    w = I.make_workload(cfg)
+    P = _prefix_len(w)
+    kc_ref, vc_ref = oracle_pools(w)
+    ref = oracle_decode(w, kc_ref, vc_ref)
+    kc, vc = gpu_pools(w)
+    for pps, PS in ((32, None), (64, -5)):
+        _say(f"[shared prefix] many rows B={cfg.B} prefix {P} partition {pps} PS={PS}")
+        got = _run(w, kc, vc, P, pps, PS=PS)
+        assert max_err(got, ref) <= tolerance(cfg), (pps, PS)
