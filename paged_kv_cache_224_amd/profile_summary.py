@@ -152,10 +152,17 @@ def _bench_args(workload: str, schedule: str, bench_args: str = "") -> str:
     return bench_args or f"--workload {workload} --schedule {schedule} --no-cpu-baseline"
 
 
+# A second pass: VALU activity, MFMA/VALU co-execution, waits of any cause, LDS activity.
+SQ_COUNTERS2 = ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_ANY",
+                "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_BUSY_CU_CYCLES",
+                "GRBM_GUI_ACTIVE"]
+
+
 def sq_commands(workload: str, schedule: str, out: str = "OUT", bench_args: str = "") -> list:
-    """The one counter pass that sq_summary() reads."""
-    return [f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {out}/sq -o run -- python -u bench.py "
-            f"{_bench_args(workload, schedule, bench_args)} --steps 5 --warmup 2"]
+    """The two counter passes that sq_summary() reads."""
+    run = f"python -u bench.py {_bench_args(workload, schedule, bench_args)} --steps 5 --warmup 2"
+    return [f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {out}/sq -o run -- {run}",
+            f"rocprofv3 --pmc {' '.join(SQ_COUNTERS2)} --output-format csv -d {out}/sq2 -o run -- {run}"]
 
 
 def _per_kernel(path: str):
@@ -172,9 +179,11 @@ def _per_kernel(path: str):
 
 def sq_summary(out: str, workload: str, schedule: str = "balanced", bench_args: str = "", name: str = "") -> str:
     """profiles/counters_<name or schedule_workload>.md: per kernel of the step, instructions per
-    wave, the MFMA pipe's busy share per SIMD, the share of wave cycles spent waiting, LDS bank
-    conflicts."""
+    wave, the MFMA pipe's and the VALU's busy shares per SIMD, MFMA/VALU co-execution, the shares
+    of wave cycles spent waiting, LDS bank conflicts."""
     vals, meta = _per_kernel(os.path.join(out, "sq", "run_counter_collection.csv"))
+    p2 = os.path.join(out, "sq2", "run_counter_collection.csv")
+    vals2 = _per_kernel(p2)[0] if os.path.exists(p2) else {}
     name = name or f"{schedule}_{workload}"
     lines = [f"# {workload}: core counters of the benchmark step ({bench_args or schedule + ' schedule'})", "",
              f"Kernel source sha256[:16] = `{source_hash()}` (paged_kv_cache_224_amd/csrc/pagedkv.hip without "
@@ -185,12 +194,22 @@ def sq_summary(out: str, workload: str, schedule: str = "balanced", bench_args: 
              "Means over the dispatches of the run.  Counters are summed over the whole GPU.  Definitions:",
              "- per wave: an instruction count / (grid threads / 64);",
              "- MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), the share of the CUs' busy "
-             "cycles in which a SIMD's matrix pipe works;",
-             "- waiting: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share of wave cycles spent waiting for an operand "
-             "or a counter;",
-             "- LDS bank conflicts: SQ_LDS_BANK_CONFLICT, cycles stalled on conflicts (whole GPU).", "",
-             "| kernel | waves | MFMA / wave | VALU / wave | LDS / wave | MFMA busy per SIMD | waiting | "
-             "LDS bank-conflict cycles |", "|---|---|---|---|---|---|---|---|"]
+             "cycles in which a SIMD's matrix pipe works (SQ_BUSY_CU_CYCLES counts CU-cycles; one "
+             "v_mfma_f32_16x16x32 occupies the pipe for 16 cycles);",
+             "- VALU busy per SIMD: SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES (quad-cycles that waves spend on VALU "
+             "instructions, x 4, per SIMD-cycle; waves sharing a SIMD are counted separately, so the share can pass "
+             "100%);",
+             "- MFMA/VALU co-exec: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES, the share of the matrix "
+             "pipe's busy cycles in which a vector instruction issued beside it;",
+             "- waiting to issue: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share of wave cycles spent waiting for an "
+             "instruction to issue; waiting (any): SQ_WAIT_ANY / SQ_WAVE_CYCLES, waiting for anything (issue, "
+             "memory counters, barriers);",
+             "- LDS bank conflicts: SQ_LDS_BANK_CONFLICT, cycles stalled on conflicts (whole GPU).",
+             "- The second group of columns comes from a second pass (the second command); a kernel's rows in the "
+             "two passes are separate runs of the same step.", "",
+             "| kernel | waves | MFMA / wave | VALU / wave | LDS / wave | MFMA busy per SIMD | VALU busy per SIMD | "
+             "MFMA/VALU co-exec | waiting to issue | waiting (any) | LDS bank-conflict cycles |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in sorted(vals):
         m = {c: sum(v) / len(v) for c, v in vals[k].items()}
         waves = max(1, meta[k] // 64)
@@ -198,9 +217,15 @@ def sq_summary(out: str, workload: str, schedule: str = "balanced", bench_args: 
         mfma_busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * busy) if busy else 0.0
         wc = m.get("SQ_WAVE_CYCLES", 0.0)
         wait = m.get("SQ_WAIT_INST_ANY", 0.0) / wc if wc else 0.0
+        m2 = {c: sum(v) / len(v) for c, v in vals2.get(k, {}).items()}
+        busy2, wc2, mb2 = m2.get("SQ_BUSY_CU_CYCLES", 0.0), m2.get("SQ_WAVE_CYCLES", 0.0), m2.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        valu = f"{100 * m2['SQ_ACTIVE_INST_VALU'] / busy2:.1f}%" if busy2 and "SQ_ACTIVE_INST_VALU" in m2 else "-"
+        coex = f"{100 * m2.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0.0) / mb2:.1f}%" if mb2 else "-"
+        wany = f"{100 * m2.get('SQ_WAIT_ANY', 0.0) / wc2:.1f}%" if wc2 else "-"
         lines.append(f"| {k[:80]} | {waves} | {m.get('SQ_INSTS_MFMA', 0) / waves:.0f} | "
                      f"{m.get('SQ_INSTS_VALU', 0) / waves:.0f} | {m.get('SQ_INSTS_LDS', 0) / waves:.0f} | "
-                     f"{100 * mfma_busy:.1f}% | {100 * wait:.1f}% | {m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+                     f"{100 * mfma_busy:.1f}% | {valu} | {coex} | {100 * wait:.1f}% | {wany} | "
+                     f"{m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
     lines.append("")
     text = "\n".join(lines)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
