@@ -13,6 +13,11 @@ Functions:
   lse_merge(...)       log-sum-exp merge of partials
   kv_write(...)        byte-exact scatter of new K/V rows into pool slots (fp8 quantising)
   fp8_encode / fp8_decode   OCP E4M3FN codec (fp32 division, nearest-even, saturating)
+  quantize_pool(...)   a whole pool through the codec
+  attn_multi_query(...)  L new tokens per sequence, causal among themselves (loops over attn)
+  copy_blocks(...)     whole-block copies (copy-on-write), reading the pools as before the call
+  swap_blocks(...)     whole blocks between the device pools and host pools, either direction
+The host block manager's reference model is ``oracle/block_manager.py``.
 """
 from __future__ import annotations
 
