@@ -143,3 +143,25 @@ def test_many_rows_merge_straddling_sequences():
         _say(f"[mq many rows] PS={PS}")
         got = _run(w, q, PS, cfg.max_len, kc, vc)
         assert max_err(got, ref) <= tolerance(cfg), PS
+
+
+@pytest.mark.parametrize("L", [1024, 4096])
+def test_prefill_chunk_lengths(L):
+    """q_len up to the 4096 the header allows (a prefill chunk): 4096 (head, new token) columns per
+    KV group, i.e. 32 column blocks.  Contexts longer than L, a few tokens shorter (its first new
+    tokens see nothing: zero rows) and much shorter, in the balanced, fixed and single-pass
+    schedules."""
+    cfg = I.Config("mq_chunk", 61, B=3, Hq=4, Hkv=1, D=128, block_size=16, q_dtype="bf16", kv_dtype="bf16",
+                   lens=("uniform", 1, 1), pool=("factor", 1.25), max_len=L + 100, partition_size=512)
+    lens = [L + 100, L - 7, 300]
+    w = I.permute_blocks(I.dense_workload(cfg, lens, seed=62), seed=63)
+    q = I.multi_query_q(cfg, L, seed=64)
+    kc_ref, vc_ref = oracle_pools(w)
+    ref = _oracle(w, q, kc_ref, vc_ref)
+    kc, vc = gpu_pools(w)
+    for PS in (_mq_split(cfg, L), 512, 0):
+        _say(f"[mq-tiled chunk] L={L} PS={PS}")
+        got = _run(w, q, PS, cfg.max_len, kc, vc)
+        assert max_err(got, ref) <= tolerance(cfg), PS
+        for b, n in enumerate(lens):
+            assert np.all(got[b, :max(0, L - n)] == 0), (b, n)
